@@ -1,0 +1,279 @@
+"""fp64 CPU oracle of the CSA2 decode-time sparse attention path.
+
+TEST INFRASTRUCTURE ONLY: used by ``tests/``, by ``__graft_entry__.smoke()`` and by the
+``cpu_baseline`` leg of ``bench.py``; nothing in the product path imports it.  It shares
+no code with the HIP library or with the input generator: it receives plain numpy arrays
+(raw cache bytes, bf16 bit patterns, fp32 weights and integer offsets) and decodes them
+itself.
+
+Sources (web pages, cited by title and section):
+  [SGL] "DeepSeek-V4.1 Flash on SGLang: from 35 to 873 tokens/s" (sglang.io blog)
+        - "Architecture changes and KV cache compression": global entries are pooled
+          two tokens per entry (one per token in the last cache), stored in FP4 at 288 B
+          (main KV) and 68 B (indexer key); a hierarchical candidate filter narrows the
+          indexer's search so that only the top 512 global positions enter attention.
+        - "DSpark adaptation and optimization": chosen candidate blocks expand straight
+          into a token mask; a verify step handles up to 6 rows per request.
+  [VLLM] "DeepSeek-V4.1-Flash runs 5.3x faster on vLLM after three weeks of optimization"
+        - "SWA bounded replay": the sliding-window cache is FP8 and covers the most
+          recent 128 positions.
+  [KT]  ktransformers issue "Support for Deepseek V4.1 Flash" (mirror): the indexer is
+        two-level; attention is sparse MLA.
+
+The pages fix the structure but not the arithmetic.  The definitions below complete
+them (each is restated where it is used):
+  * main entry   = 512 E2M1 codes (element 2i in the low nibble of byte i) then 32 E8M0
+                   scales, one per 16 elements (256 + 32 = 288 B);
+  * indexer key  = 128 E2M1 codes then 4 E8M0 scales, one per 32 elements (64 + 4 = 68 B);
+  * window token = 512 E4M3FN codes and one fp32 scale;
+  * index score  s_t = sum_{h<8} w_h * max(0, q_h . k_t), head dim 128;
+  * coarse stage = the same score on each 64-entry block's bf16 summary key; keep the
+                   64 best blocks (ties to the lower block) plus the newest block;
+  * fine stage   = the 512 best scores among the kept blocks' entries (ties to the
+                   lower position), reported in ascending position;
+  * attention    = MQA over the 512-dim latent (K = V = latent) for 64 heads, one
+                   softmax jointly over the selected entries and the row's window,
+                   logit scale 1/sqrt(512), no de-duplication, no sink.
+
+Every function here is pinned by tests in tests/test_formats.py and tests/test_oracle.py
+(format tables against a library decoder and the OCP MX value table, brute-force exact
+rational scores, brute-force selection, the dense-attention special case, LSE merging
+and invariants).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+D = 512            # latent dim (attention K = V)
+H = 64             # query heads
+D_IDX = 128        # indexer head dim
+H_IDX = 8          # indexer heads
+BLOCK = 64         # entries per coarse block
+MAIN_BYTES = 288
+IDX_BYTES = 68
+SCAN_CHUNK = 65536  # entries dequantised at a time (keeps 1M-entry requests in memory)
+
+
+# ---------------------------------------------------------------------------------
+# O1. Formats, decoded from their bit-field definitions.
+# ---------------------------------------------------------------------------------
+
+def e2m1_value(code: int) -> float:
+    """OCP MX FP4 E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+
+    Exponent field 0 is subnormal (0.5 * m); otherwise 2**(e-1) * (1 + m/2).  There is
+    no inf or NaN.
+    """
+    s = (code >> 3) & 1
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+    return -mag if s else mag
+
+
+def e8m0_value(u: int) -> float:
+    """OCP MX E8M0 scale: 2**(u - 127); code 255 is NaN."""
+    return math.nan if u == 255 else 2.0 ** (u - 127)
+
+
+def e4m3fn_value(c: int) -> float:
+    """OCP FP8 E4M3FN: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+
+    Exponent field 0 is subnormal (m/8 * 2**-6); exponent 15 with mantissa 7 is NaN;
+    no inf (largest finite 448).
+    """
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    if e == 15 and m == 7:
+        return math.nan
+    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+E8M0 = np.array([e8m0_value(u) for u in range(256)], dtype=np.float64)
+E4M3 = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> their exact values (bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def dequant_fp4_records(rec: np.ndarray, dim: int, block: int) -> np.ndarray:
+    """Records [n, dim/2 + dim/block] of E2M1 codes + E8M0 scales -> exact values [n, dim]."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    codes = rec[:, : dim // 2]
+    vals = np.empty((rec.shape[0], dim), dtype=np.float64)
+    vals[:, 0::2] = E2M1[codes & 0x0F]
+    vals[:, 1::2] = E2M1[codes >> 4]
+    scale = E8M0[rec[:, dim // 2: dim // 2 + dim // block]]
+    return vals * np.repeat(scale, block, axis=1)
+
+
+def dequant_main(rec: np.ndarray) -> np.ndarray:
+    """288-B main KV records -> [n, 512] (E8M0 block 16)."""
+    return dequant_fp4_records(rec, D, 16)
+
+
+def dequant_idx(rec: np.ndarray) -> np.ndarray:
+    """68-B indexer key records -> [n, 128] (E8M0 block 32)."""
+    return dequant_fp4_records(rec, D_IDX, 32)
+
+
+def dequant_swa(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """E4M3FN codes [t, 512] and fp32 scales [t] -> [t, 512] (exact in fp64)."""
+    return E4M3[np.asarray(codes, dtype=np.uint8)] * np.asarray(scale, dtype=np.float32).astype(np.float64)[:, None]
+
+
+# ---------------------------------------------------------------------------------
+# O2/O3. Indexer score, on entries and on block summaries.
+# ---------------------------------------------------------------------------------
+
+def indexer_score(q_idx: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """s_t = sum_h w_h * max(0, q_h . k_t) for every row k_t of ``keys``.
+
+    q_idx: [8, 128] exact query values, w: [8], keys: [n, 128] exact key values.
+    """
+    dots = keys @ np.asarray(q_idx, dtype=np.float64).T          # [n, 8]
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------------
+# O4. Coarse block filter.
+# ---------------------------------------------------------------------------------
+
+def keep_blocks(block_scores: np.ndarray, n_keep: int = 64, keep_newest: bool = True) -> np.ndarray:
+    """Blocks kept by the coarse stage, ascending.
+
+    With nb <= n_keep every block is kept.  Otherwise order blocks by (score desc,
+    block asc), keep the first n_keep, and add the newest block (nb-1) if it is not
+    among them.
+    """
+    nb = int(block_scores.shape[0])
+    if nb <= n_keep:
+        return np.arange(nb, dtype=np.int64)
+    order = np.lexsort((np.arange(nb), -np.asarray(block_scores, dtype=np.float64)))
+    kept = set(int(j) for j in order[:n_keep])
+    if keep_newest and nb > 0:
+        kept.add(nb - 1)
+    return np.array(sorted(kept), dtype=np.int64)
+
+
+def blocks_to_entries(kept: np.ndarray, n_entries: int) -> np.ndarray:
+    """Expand kept blocks into their entry positions (the newest block may be partial)."""
+    parts = [np.arange(BLOCK * j, min(BLOCK * (j + 1), n_entries), dtype=np.int64) for j in kept]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------------
+# O5/O6. Fine top-k.
+# ---------------------------------------------------------------------------------
+
+def top_k(positions: np.ndarray, scores: np.ndarray, k: int) -> np.ndarray:
+    """The k best (score desc, position asc) of the candidates, reported ascending."""
+    positions = np.asarray(positions, dtype=np.int64)
+    order = np.lexsort((positions, -np.asarray(scores, dtype=np.float64)))
+    return np.sort(positions[order[:k]])
+
+
+# ---------------------------------------------------------------------------------
+# O7. Joint-softmax latent attention.
+# ---------------------------------------------------------------------------------
+
+def joint_attention(q: np.ndarray, keys: np.ndarray, sm_scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """For each head h: z_i = sm_scale * q_h . x_i, out_h = sum_i softmax(z)_i x_i, lse_h.
+
+    q: [64, 512] exact query values; keys: [n, 512] exact latents (K = V).  With n = 0
+    the output is 0 and the log-sum-exp is -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros((q.shape[0], D)), np.full(q.shape[0], -np.inf)
+    z = (q @ keys.T) * float(sm_scale)                            # [64, n]
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    s = p.sum(axis=1, keepdims=True)
+    out = (p @ keys) / s
+    lse = (m + np.log(s))[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------------
+# The whole path for one workload.
+# ---------------------------------------------------------------------------------
+
+def request_scores(wl, b: int) -> np.ndarray:
+    """Index scores of every entry of request b for each of its rows: [rows_b, N_b]."""
+    r0, r1 = int(wl.row_off[b]), int(wl.row_off[b + 1])
+    e0, e1 = int(wl.entry_off[b]), int(wl.entry_off[b + 1])
+    out = np.zeros((r1 - r0, e1 - e0), dtype=np.float64)
+    qs = [bf16_value(wl.q_idx[r]) for r in range(r0, r1)]
+    for c0 in range(e0, e1, SCAN_CHUNK):
+        c1 = min(e1, c0 + SCAN_CHUNK)
+        keys = dequant_idx(wl.idx_k[c0:c1])
+        for j, r in enumerate(range(r0, r1)):
+            out[j, c0 - e0:c1 - e0] = indexer_score(qs[j], wl.w[r], keys)
+    return out
+
+
+def block_scores_row(wl, r: int) -> np.ndarray:
+    b = int(wl.row_req[r])
+    summ = bf16_value(wl.blk_sum[int(wl.block_off[b]):int(wl.block_off[b + 1])])
+    return indexer_score(bf16_value(wl.q_idx[r]), wl.w[r], summ)
+
+
+def row_keys(wl, r: int, sel: np.ndarray) -> np.ndarray:
+    """The row's attention keys: the selected main entries, then its window tokens."""
+    b = int(wl.row_req[r])
+    e0 = int(wl.entry_off[b])
+    main = dequant_main(wl.main_kv[e0 + np.asarray(sel, dtype=np.int64)])
+    s0 = int(wl.row_swa_start[r])
+    s1 = s0 + int(wl.row_swa_len[r])
+    win = dequant_swa(wl.swa[s0:s1], wl.swa_scale[s0:s1])
+    return np.concatenate([main, win], axis=0)
+
+
+def decode(wl, rows=None, k: int | None = None, n_keep: int | None = None, keep_newest: int | None = None,
+           kept_override: dict | None = None, sel_override: dict | None = None) -> list:
+    """Run the path for ``rows`` (default: all) and return one dict per row.
+
+    Each dict holds: ``kept`` (ascending blocks), ``block_scores`` [nb], ``cand``
+    (candidate positions), ``cand_scores``, ``sel`` (ascending positions), ``out``
+    [64, 512], ``lse`` [64].  ``kept_override`` / ``sel_override`` map a row to a kept
+    set / selected set to use instead of the oracle's own (to re-run the later steps on
+    another implementation's choices).
+    """
+    k = wl.k if k is None else k
+    n_keep = wl.n_keep if n_keep is None else n_keep
+    keep_newest = wl.keep_newest if keep_newest is None else keep_newest
+    R = int(wl.row_req.shape[0])
+    rows = list(range(R)) if rows is None else list(rows)
+    by_req: dict = {}
+    for r in rows:
+        by_req.setdefault(int(wl.row_req[r]), []).append(r)
+    res = {}
+    for b, rs in by_req.items():
+        n = int(wl.entry_off[b + 1] - wl.entry_off[b])
+        sc = request_scores(wl, b) if n else np.zeros((int(wl.row_off[b + 1] - wl.row_off[b]), 0))
+        for r in rs:
+            s = sc[r - int(wl.row_off[b])]
+            bs = block_scores_row(wl, r)
+            if kept_override is not None and r in kept_override:
+                kept = np.asarray(kept_override[r], dtype=np.int64)
+            else:
+                kept = keep_blocks(bs, n_keep, bool(keep_newest))
+            cand = blocks_to_entries(kept, n)
+            cs = s[cand]
+            if sel_override is not None and r in sel_override:
+                sel = np.asarray(sel_override[r], dtype=np.int64)
+            else:
+                sel = top_k(cand, cs, k)
+            out, lse = joint_attention(bf16_value(wl.q[r]), row_keys(wl, r, sel), wl.sm_scale)
+            res[r] = dict(kept=kept, block_scores=bs, cand=cand, cand_scores=cs, scores=s, sel=sel,
+                          out=out, lse=lse)
+    return [res[r] for r in rows]

@@ -1,0 +1,264 @@
+"""Pins for the oracle's scoring, selection and attention against brute force, library
+routines, closed forms and invariants (no GPU)."""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from synth import make_workload
+
+E2M1_FRAC = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+             Fraction(6)]
+
+
+def _fp4_record_fractions(rec, dim, block):
+    """Independent exact decode: nibble values from the OCP table, scales via torch's E8M0."""
+    scales = torch.from_numpy(rec[dim // 2:].copy()).view(torch.float8_e8m0fnu).double().tolist()
+    out = []
+    for j in range(dim):
+        byte = int(rec[j // 2])
+        c = (byte >> 4) if j % 2 else (byte & 15)
+        v = E2M1_FRAC[c & 7] * Fraction(scales[j // block])
+        out.append(-v if c & 8 else v)
+    return out
+
+
+def _bf16_fractions(bits):
+    t = torch.from_numpy(np.asarray(bits, dtype=np.uint16).view(np.int16).copy()).view(torch.bfloat16).double()
+    return [Fraction(v) for v in t.flatten().tolist()]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    # 3 requests: 130 entries (3 blocks, last partial), 64, 1 entry; 2 rows on the first.
+    return make_workload("t", 123, [130, 64, 1], rows_per_req=[2, 1, 1], n_needles=4)
+
+
+def test_index_score_bruteforce_exact(tiny):
+    wl = tiny
+    for r in range(wl.num_rows):
+        b = int(wl.row_req[r])
+        e0, e1 = int(wl.entry_off[b]), int(wl.entry_off[b + 1])
+        q = _bf16_fractions(wl.q_idx[r])
+        w = [Fraction(float(x)) for x in wl.w[r]]
+        got = oracle.request_scores(wl, b)[r - int(wl.row_off[b])]
+        for t in range(0, e1 - e0, 7):
+            k = _fp4_record_fractions(wl.idx_k[e0 + t], 128, 32)
+            s = Fraction(0)
+            for h in range(8):
+                dot = sum(q[h * 128 + d] * k[d] for d in range(128))
+                s += w[h] * max(Fraction(0), dot)
+            assert abs(got[t] - float(s)) <= 1e-12 * max(1.0, abs(float(s))), (r, t)
+
+
+def test_block_score_bruteforce_exact(tiny):
+    wl = tiny
+    for r in range(wl.num_rows):
+        b = int(wl.row_req[r])
+        q = _bf16_fractions(wl.q_idx[r])
+        w = [Fraction(float(x)) for x in wl.w[r]]
+        got = oracle.block_scores_row(wl, r)
+        for j in range(int(wl.block_off[b]), int(wl.block_off[b + 1])):
+            k = _bf16_fractions(wl.blk_sum[j])
+            s = sum(w[h] * max(Fraction(0), sum(q[h * 128 + d] * k[d] for d in range(128))) for h in range(8))
+            assert abs(got[j - int(wl.block_off[b])] - float(s)) <= 1e-12 * max(1.0, abs(float(s)))
+
+
+def test_index_score_single_head_is_relu_dot():
+    rng = np.random.default_rng(3)
+    q = np.zeros((8, 128))
+    q[2] = rng.standard_normal(128)
+    w = np.zeros(8)
+    w[2] = 1.0
+    keys = rng.standard_normal((50, 128))
+    got = oracle.indexer_score(q, w, keys)
+    ref = np.array([max(0.0, float(np.dot(q[2], k))) for k in keys])
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-14)
+
+
+def _brute_topk(pos, sc, k):
+    # Repeated selection of the best remaining (score desc, position asc).
+    left = list(zip(pos.tolist(), sc.tolist()))
+    out = []
+    for _ in range(min(k, len(left))):
+        best = None
+        for i, (p, s) in enumerate(left):
+            if best is None or s > left[best][1] or (s == left[best][1] and p < left[best][0]):
+                best = i
+        out.append(left.pop(best)[0])
+    return sorted(out)
+
+
+def test_topk_bruteforce_with_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        n = int(rng.integers(1, 90))
+        pos = np.sort(rng.choice(1000, size=n, replace=False))
+        sc = rng.integers(0, 6, size=n).astype(np.float64)        # many exact ties
+        k = int(rng.integers(1, 100))
+        assert oracle.top_k(pos, sc, k).tolist() == _brute_topk(pos, sc, k)
+
+
+def test_topk_k_at_least_candidates_returns_all():
+    pos = np.array([5, 1, 9, 3])
+    assert oracle.top_k(pos, np.array([0.1, 0.2, 0.3, 0.4]), 512).tolist() == [1, 3, 5, 9]
+
+
+def test_keep_blocks_rules():
+    # nb <= n_keep: identity.
+    assert oracle.keep_blocks(np.arange(64.0), 64).tolist() == list(range(64))
+    # The newest block is kept even with the lowest score.
+    s = np.arange(100.0, 0.0, -1.0)                 # block 99 has the lowest score
+    kept = oracle.keep_blocks(s, 64)
+    assert kept.tolist() == list(range(64)) + [99]
+    # Newest already in the top 64: exactly 64 kept.
+    s2 = s.copy()
+    s2[99] = 1000.0
+    assert oracle.keep_blocks(s2, 64).tolist() == list(range(63)) + [99]
+    # Ties go to the lower block.
+    s3 = np.zeros(100)
+    assert oracle.keep_blocks(s3, 64).tolist() == list(range(64)) + [99]
+    assert oracle.keep_blocks(s3, 64, keep_newest=False).tolist() == list(range(64))
+
+
+def test_keep_blocks_bruteforce():
+    rng = np.random.default_rng(9)
+    for _ in range(30):
+        nb = int(rng.integers(1, 200))
+        s = rng.integers(0, 10, size=nb).astype(float)
+        ref = sorted(range(nb), key=lambda j: (-s[j], j))
+        ref = set(ref[:64]) if nb > 64 else set(range(nb))
+        ref.add(nb - 1)
+        assert oracle.keep_blocks(s, 64).tolist() == sorted(ref)
+
+
+def test_blocks_to_entries_partial_newest():
+    assert oracle.blocks_to_entries(np.array([0, 2]), 130).tolist() == list(range(64)) + [128, 129]
+
+
+def _sdpa(q, x, scale):
+    # torch's reference attention in float64 on the CPU (K = V = x, one query per head).
+    qt = torch.from_numpy(q)[None, :, None, :]              # [1, H, 1, D]
+    kt = torch.from_numpy(x)[None, None].expand(1, q.shape[0], x.shape[0], x.shape[1])
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=scale)
+    return o[0, :, 0].numpy()
+
+
+def test_attention_matches_library_routines():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((64, 512))
+    x = rng.standard_normal((300, 512))
+    out, lse = oracle.joint_attention(q, x, 1 / math.sqrt(512))
+    assert np.allclose(out, _sdpa(q, x, 1 / math.sqrt(512)), rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, scipy.special.logsumexp((q @ x.T) / math.sqrt(512), axis=1), rtol=1e-13)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((10, 512))
+    # Single key: output is the key, lse is its logit.
+    q = rng.standard_normal((64, 512))
+    out, lse = oracle.joint_attention(q, x[:1], 0.1)
+    assert np.allclose(out, np.broadcast_to(x[0], out.shape), rtol=0, atol=1e-15)
+    assert np.allclose(lse, 0.1 * q @ x[0])
+    # All-equal logits (q = 0): output is the mean of the keys, lse = log n.
+    out, lse = oracle.joint_attention(np.zeros((64, 512)), x, 0.1)
+    assert np.allclose(out, x.mean(axis=0)[None], atol=1e-14)
+    assert np.allclose(lse, math.log(10))
+    # No keys: zeros and -inf.
+    out, lse = oracle.joint_attention(q, x[:0], 0.1)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_attention_lse_merge_and_permutation():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((64, 512))
+    a = rng.standard_normal((40, 512))
+    b = rng.standard_normal((25, 512)) * 2
+    s = 1 / math.sqrt(512)
+    oa, la = oracle.joint_attention(q, a, s)
+    ob, lb = oracle.joint_attention(q, b, s)
+    oj, lj = oracle.joint_attention(q, np.concatenate([a, b]), s)
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    assert np.allclose(oj, (wa[:, None] * oa + wb[:, None] * ob) / (wa + wb)[:, None], rtol=1e-12, atol=1e-13)
+    assert np.allclose(lj, m + np.log(wa + wb), rtol=1e-13)
+    perm = rng.permutation(65)
+    op, lp = oracle.joint_attention(q, np.concatenate([a, b])[perm], s)
+    assert np.allclose(op, oj, rtol=1e-12, atol=1e-13) and np.allclose(lp, lj)
+
+
+def test_decode_keep_all_equals_dense_attention():
+    # With k >= N and the coarse stage keeping every block, the path is dense attention
+    # over all of the request's entries plus the row's window.
+    wl = make_workload("dense", 31, [300, 97], rows_per_req=[2, 1], n_needles=3, swa_len=[128, 40])
+    res = oracle.decode(wl, k=4096, n_keep=1000)
+    for r, rr in enumerate(res):
+        b = int(wl.row_req[r])
+        n = wl.n_entries(b)
+        assert rr["sel"].tolist() == list(range(n))
+        e0 = int(wl.entry_off[b])
+        main = torch.from_numpy(wl.main_kv[e0:e0 + n].copy())
+        # Independent decode of the main records via the OCP table and torch's E8M0/E4M3 decoders.
+        x = np.array([[float(v) for v in _fp4_record_fractions(main[i].numpy(), 512, 16)] for i in range(n)])
+        s0, sl = int(wl.row_swa_start[r]), int(wl.row_swa_len[r])
+        win = torch.from_numpy(wl.swa[s0:s0 + sl].copy()).view(torch.float8_e4m3fn).double().numpy()
+        win = win * wl.swa_scale[s0:s0 + sl].astype(np.float64)[:, None]
+        keys = np.concatenate([x, win])
+        q = torch.from_numpy(wl.q[r].view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+        assert np.allclose(rr["out"], _sdpa(q, keys, wl.sm_scale), rtol=1e-11, atol=1e-12)
+        lse = scipy.special.logsumexp((q @ keys.T) * wl.sm_scale, axis=1)
+        assert np.allclose(rr["lse"], lse, rtol=1e-12)
+
+
+def test_decode_selection_composes_steps():
+    # One row over 40 blocks with a small k: the oracle's selection equals brute force on
+    # the candidates of its own coarse stage, and the coarse stage equals brute force on
+    # block scores computed independently.
+    wl = make_workload("sel", 77, [2560 + 17], rows_per_req=1, n_needles=8)
+    rr = oracle.decode(wl, k=100, n_keep=10)[0]
+    bs = oracle.block_scores_row(wl, 0)
+    order = sorted(range(len(bs)), key=lambda j: (-bs[j], j))[:10]
+    assert rr["kept"].tolist() == sorted(set(order) | {len(bs) - 1})
+    cand = [t for t in range(wl.n_entries(0)) if t // 64 in set(rr["kept"].tolist())]
+    assert rr["cand"].tolist() == cand
+    assert rr["sel"].tolist() == _brute_topk(np.array(cand), rr["scores"][cand], 100)
+
+
+def test_needles_rank_high_when_kept():
+    # Needle keys are 3x the mean indexer query, so their scores exceed typical entries.
+    wl = make_workload("needle", 5, [2048], rows_per_req=1, n_needles=16)
+    rr = oracle.decode(wl)[0]
+    assert set(wl.needles[0].tolist()) <= set(rr["sel"].tolist())
+
+
+def test_empty_and_degenerate_requests():
+    wl = make_workload("edge", 8, [0, 1, 63, 64, 65], rows_per_req=1, n_needles=1, swa_len=[0, 1, 128, 5, 0])
+    res = oracle.decode(wl)
+    assert res[0]["sel"].size == 0 and np.all(np.isneginf(res[0]["lse"]))
+    assert res[1]["sel"].tolist() == [0]
+    assert res[2]["sel"].tolist() == list(range(63))
+    assert res[4]["kept"].tolist() == [0, 1] and res[4]["sel"].tolist() == list(range(65))
+    for rr in res[1:]:
+        assert np.all(np.isfinite(rr["out"])) and np.all(np.isfinite(rr["lse"]))
+
+
+def test_generator_is_deterministic():
+    a = make_workload("d", 3, [1000, 70], rows_per_req=[1, 2])
+    b = make_workload("d", 3, [1000, 70], rows_per_req=[1, 2], workers=1)
+    for f in ("idx_k", "main_kv", "blk_sum", "swa", "swa_scale", "q", "q_idx", "w"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+
+
+@pytest.mark.parametrize("i", [0])
+def test_config0_oracle_runs(i):
+    from synth import make_config
+    wl = make_config(i)
+    rr = oracle.decode(wl)[0]
+    assert rr["sel"].size == 512 and rr["kept"].size == 32
+    assert np.all(np.isfinite(rr["out"]))
