@@ -1,0 +1,459 @@
+// Host entry points of libcsa2: argument checks, workspace layout, launch chains.
+// Every check runs before any launch; nothing here synchronises or allocates.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "csa2_internal.h"
+
+using namespace csa2;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(CSA2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_ragged(const csa2_ragged* rg, RaggedDev& g) {
+  if (!rg) return fail(CSA2_ERR_INVALID_ARG, "ragged descriptor is NULL");
+  if (rg->num_requests < 0 || rg->num_rows < 0) return fail(CSA2_ERR_INVALID_ARG, "negative request/row count");
+  if (rg->num_requests > 65535 || rg->num_rows > 65535)
+    return fail(CSA2_ERR_UNSUPPORTED, "at most 65535 requests and 65535 rows per call");
+  if (rg->num_rows > 0 && rg->num_requests == 0) return fail(CSA2_ERR_INVALID_ARG, "rows without requests");
+  if (rg->num_requests > 0 && (!rg->entry_off || !rg->block_off || !rg->row_off))
+    return fail(CSA2_ERR_INVALID_ARG, "entry_off/block_off/row_off is NULL");
+  if (rg->num_rows > 0 && (!rg->row_req || !rg->row_swa_start || !rg->row_swa_len))
+    return fail(CSA2_ERR_INVALID_ARG, "row_req/row_swa_start/row_swa_len is NULL");
+  if (rg->max_entries < 0 || rg->total_entries < 0 || rg->total_blocks < 0 || rg->swa_tokens < 0)
+    return fail(CSA2_ERR_INVALID_ARG, "negative pool size");
+  if (rg->max_entries > rg->total_entries)
+    return fail(CSA2_ERR_INVALID_ARG, "max_entries %lld exceeds total_entries %lld", (long long)rg->max_entries,
+                (long long)rg->total_entries);
+  if (rg->max_entries >= (int64_t(1) << 31)) return fail(CSA2_ERR_UNSUPPORTED, "max_entries must be < 2^31");
+  if (rg->num_rows > 0 && (rg->max_rows_per_request < 1 || rg->max_rows_per_request > CSA2_ROWS_PER_REQ_MAX))
+    return fail(CSA2_ERR_UNSUPPORTED, "max_rows_per_request must be in 1..%d", CSA2_ROWS_PER_REQ_MAX);
+  g.entry_off = rg->entry_off;
+  g.block_off = rg->block_off;
+  g.row_off = rg->row_off;
+  g.row_req = rg->row_req;
+  g.row_swa_start = rg->row_swa_start;
+  g.row_swa_len = rg->row_swa_len;
+  g.max_entries = rg->max_entries;
+  g.total_entries = rg->total_entries;
+  g.total_blocks = rg->total_blocks;
+  g.swa_tokens = rg->swa_tokens;
+  g.B = rg->num_requests;
+  g.R = rg->num_rows;
+  return CSA2_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(CSA2_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(CSA2_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return CSA2_OK;
+}
+
+#define CHECK(expr)            \
+  do {                         \
+    int _rc = (expr);          \
+    if (_rc != CSA2_OK) return _rc; \
+  } while (0)
+
+#define LAUNCH(expr, where)                     \
+  do {                                          \
+    hipError_t _e = (expr);                     \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+int64_t blocks_of(int64_t entries) { return ceil_div(entries, CSA2_BLOCK); }
+
+// Workspace carve-out: a bump allocator over the caller's buffer.
+struct Carve {
+  char* base;
+  size_t used;
+  template <typename T>
+  T* take(size_t count) {
+    used = round_up(used, 256);
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// Test hook: the kernels' dequantisation helpers over raw records.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n,
+                                                      float* out) {
+  const int groups = (kind == CSA2_DQ_IDX) ? CSA2_IDX_D / 8 : CSA2_D / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n * groups) return;
+  const int64_t i = t / groups;
+  const int grp = (int)(t % groups);
+  float v[8];
+  if (kind == CSA2_DQ_MAIN) {
+    const uint8_t* p = rec + i * CSA2_MAIN_BYTES;
+    const uint32_t codes = *reinterpret_cast<const uint32_t*>(p + 4 * grp);
+    bf16x8_words_to_f32(fp4x8_to_bf16(codes, e8m0_operand(p[256 + grp / 2])), v);
+  } else if (kind == CSA2_DQ_IDX) {
+    const uint8_t* p = rec + i * CSA2_IDX_BYTES;
+    const uint32_t codes = *reinterpret_cast<const uint32_t*>(p + 4 * grp);
+    bf16x8_words_to_f32(fp4x8_to_bf16(codes, e8m0_operand(p[64 + grp / 4])), v);
+  } else {
+    const uint8_t* p = rec + i * CSA2_D + 8 * grp;
+    const bf16x4_t lo = e4m3x4_to_bf16(*reinterpret_cast<const uint32_t*>(p));
+    const bf16x4_t hi = e4m3x4_to_bf16(*reinterpret_cast<const uint32_t*>(p + 4));
+    bf16x8_words_to_f32(bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, v);
+    const float s = scales[i];
+    for (int j = 0; j < 8; ++j) v[j] *= s;
+  }
+  const int dim = (kind == CSA2_DQ_IDX) ? CSA2_IDX_D : CSA2_D;
+  for (int j = 0; j < 8; ++j) out[i * dim + 8 * grp + j] = v[j];
+}
+
+}  // namespace
+
+namespace csa2 {
+hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
+                                hipStream_t st) {
+  const int groups = (kind == CSA2_DQ_IDX) ? CSA2_IDX_D / 8 : CSA2_D / 8;
+  const int64_t threads = n * groups;
+  if (threads == 0) return hipSuccess;
+  k_debug_dequant<<<dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, st>>>(kind, rec, scales, n, out);
+  return hipGetLastError();
+}
+}  // namespace csa2
+
+// =================================================================================
+// C ABI
+// =================================================================================
+extern "C" {
+
+int csa2_index_score(const csa2_ragged* rg, const uint8_t* idx_k, const uint16_t* q_idx, const float* w_idx,
+                     const int32_t* kept_blocks, const int32_t* n_kept, int32_t kept_ld, float* scores, int64_t ld,
+                     void* stream) {
+  RaggedDev g;
+  CHECK(check_ragged(rg, g));
+  if (g.R == 0) return CSA2_OK;
+  CHECK(check_ptr(idx_k, 4, "idx_k"));
+  CHECK(check_ptr(q_idx, 16, "q_idx"));
+  CHECK(check_ptr(w_idx, 4, "w_idx"));
+  CHECK(check_ptr(scores, 4, "scores"));
+  if (ld < g.max_entries || ld < 1) return fail(CSA2_ERR_INVALID_ARG, "ld %lld < max_entries", (long long)ld);
+  ScanArgs a{};
+  a.g = g;
+  a.idx_k = idx_k;
+  a.q_idx = q_idx;
+  a.w = w_idx;
+  a.scores = scores;
+  a.ld = ld;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (kept_blocks) {
+    if (!n_kept) return fail(CSA2_ERR_INVALID_ARG, "n_kept is NULL");
+    if (kept_ld < 1 || kept_ld > 65535) return fail(CSA2_ERR_INVALID_ARG, "kept_ld must be in 1..65535");
+    a.kept = kept_blocks;
+    a.n_kept = n_kept;
+    a.kept_ld = kept_ld;
+    LAUNCH(launch_scan_kept(a, st), "index scan (kept blocks)");
+  } else {
+    LAUNCH(launch_scan(a, rg->max_rows_per_request, true, false, st), "index scan");
+  }
+  return CSA2_OK;
+}
+
+int csa2_block_filter(const csa2_ragged* rg, const uint16_t* blk_sum, const uint16_t* q_idx, const float* w_idx,
+                      int32_t n_keep, int32_t keep_newest, int32_t* kept_blocks, int32_t* n_kept, float* blk_scores,
+                      int64_t blk_ld, void* stream) {
+  RaggedDev g;
+  CHECK(check_ragged(rg, g));
+  if (n_keep < 1 || n_keep > CSA2_KEEP_MAX) return fail(CSA2_ERR_UNSUPPORTED, "n_keep must be in 1..%d", CSA2_KEEP_MAX);
+  if (g.R == 0) return CSA2_OK;
+  CHECK(check_ptr(blk_sum, 16, "blk_sum"));
+  CHECK(check_ptr(q_idx, 16, "q_idx"));
+  CHECK(check_ptr(w_idx, 4, "w_idx"));
+  CHECK(check_ptr(kept_blocks, 4, "kept_blocks"));
+  CHECK(check_ptr(n_kept, 4, "n_kept"));
+  CHECK(check_ptr(blk_scores, 4, "blk_scores"));
+  if (blk_ld < blocks_of(g.max_entries) || blk_ld < 1)
+    return fail(CSA2_ERR_INVALID_ARG, "blk_ld must be >= ceil(max_entries/64)");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  ScanArgs a{};
+  a.g = g;
+  a.blk_sum = blk_sum;
+  a.q_idx = q_idx;
+  a.w = w_idx;
+  a.blk_scores = blk_scores;
+  a.blk_ld = blk_ld;
+  LAUNCH(launch_scan(a, rg->max_rows_per_request, false, true, st), "block scores");
+  SelectArgs s{};
+  s.g = g;
+  s.blk_scores = blk_scores;
+  s.blk_ld = blk_ld;
+  s.n_keep = n_keep;
+  s.keep_newest = keep_newest ? 1 : 0;
+  s.kept = kept_blocks;
+  s.n_kept = n_kept;
+  s.kept_ld = n_keep + 1;
+  LAUNCH(launch_block_select(s, st), "block select");
+  return CSA2_OK;
+}
+
+int csa2_topk(const csa2_ragged* rg, const float* scores, int64_t ld, const int32_t* kept_blocks,
+              const int32_t* n_kept, int32_t kept_ld, int32_t k, int32_t* sel_idx, int32_t* n_sel, float* sel_score,
+              void* stream) {
+  RaggedDev g;
+  CHECK(check_ragged(rg, g));
+  if (k < 1 || k > CSA2_K_MAX) return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d", CSA2_K_MAX);
+  if (g.R == 0) return CSA2_OK;
+  CHECK(check_ptr(scores, 4, "scores"));
+  CHECK(check_ptr(sel_idx, 4, "sel_idx"));
+  CHECK(check_ptr(n_sel, 4, "n_sel"));
+  if (sel_score) CHECK(check_ptr(sel_score, 4, "sel_score"));
+  if (ld < g.max_entries || ld < 1) return fail(CSA2_ERR_INVALID_ARG, "ld < max_entries");
+  if (kept_blocks) {
+    if (!n_kept) return fail(CSA2_ERR_INVALID_ARG, "n_kept is NULL");
+    if (kept_ld < 1) return fail(CSA2_ERR_INVALID_ARG, "kept_ld must be >= 1");
+  } else if (g.max_entries > CSA2_TOPK_ALL_MAX) {
+    return fail(CSA2_ERR_UNSUPPORTED, "without kept blocks, max_entries must be <= %d", CSA2_TOPK_ALL_MAX);
+  }
+  SelectArgs s{};
+  s.g = g;
+  s.kept = const_cast<int32_t*>(kept_blocks);
+  s.n_kept = const_cast<int32_t*>(n_kept);
+  s.kept_ld = kept_ld;
+  s.scores = scores;
+  s.ld = ld;
+  s.k = k;
+  s.sel = sel_idx;
+  s.n_sel = n_sel;
+  s.sel_score = sel_score;
+  LAUNCH(launch_topk(s, kept_blocks == nullptr, reinterpret_cast<hipStream_t>(stream)), "top-k");
+  return CSA2_OK;
+}
+
+size_t csa2_sparse_attn_workspace_size(const csa2_ragged* rg, int32_t sel_ld) {
+  if (!rg || rg->num_rows <= 0 || sel_ld < 1) return 0;
+  return attn_workspace_bytes(rg->num_rows, sel_ld);
+}
+
+static int attn_args(const RaggedDev& g, const uint16_t* q, const uint8_t* main_kv, const int32_t* sel_idx,
+                     const int32_t* n_sel, int32_t sel_ld, const uint8_t* swa, const float* swa_scale, float sm_scale,
+                     float* out, float* lse, void* ws, size_t ws_bytes, AttnArgs& a) {
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(main_kv, 16, "main_kv"));
+  CHECK(check_ptr(sel_idx, 4, "sel_idx"));
+  CHECK(check_ptr(n_sel, 4, "n_sel"));
+  CHECK(check_ptr(out, 16, "out"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  if (g.swa_tokens > 0) {
+    CHECK(check_ptr(swa, 16, "swa"));
+    CHECK(check_ptr(swa_scale, 4, "swa_scale"));
+  }
+  if (sel_ld < 1 || sel_ld > CSA2_K_MAX) return fail(CSA2_ERR_UNSUPPORTED, "sel_ld must be in 1..%d", CSA2_K_MAX);
+  if (!isfinite(sm_scale)) return fail(CSA2_ERR_INVALID_ARG, "sm_scale is not finite");
+  a.g = g;
+  a.q = q;
+  a.main_kv = main_kv;
+  a.sel = sel_idx;
+  a.n_sel = n_sel;
+  a.sel_ld = sel_ld;
+  a.swa = swa;
+  a.swa_scale = swa_scale;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  attn_plan(g.R, sel_ld, a.tiles_per_split, a.splits);
+  const size_t need = attn_workspace_bytes(g.R, sel_ld);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(CSA2_ERR_WORKSPACE_TOO_SMALL, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (!aligned(ws, 256)) return fail(CSA2_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    Carve c{static_cast<char*>(ws), 0};
+    const size_t parts = (size_t)g.R * a.splits * CSA2_HEADS;
+    a.opart = c.take<float>(parts * CSA2_D);
+    a.mpart = c.take<float>(parts);
+    a.lpart = c.take<float>(parts);
+  }
+  return CSA2_OK;
+}
+
+int csa2_sparse_attn(const csa2_ragged* rg, const uint16_t* q, const uint8_t* main_kv, const int32_t* sel_idx,
+                     const int32_t* n_sel, int32_t sel_ld, const uint8_t* swa, const float* swa_scale, float sm_scale,
+                     float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  RaggedDev g;
+  CHECK(check_ragged(rg, g));
+  if (g.R == 0) return CSA2_OK;
+  AttnArgs a{};
+  CHECK(attn_args(g, q, main_kv, sel_idx, n_sel, sel_ld, swa, swa_scale, sm_scale, out, lse, ws, ws_bytes, a));
+  LAUNCH(launch_attn(a, reinterpret_cast<hipStream_t>(stream)), "sparse attention");
+  return CSA2_OK;
+}
+
+// Workspace of csa2_decode, in carve order.
+static size_t decode_layout(const csa2_decode_args* a, char* base, float** scores, float** blk_scores,
+                            int32_t** kept, int32_t** n_kept, int32_t** sel, int32_t** n_sel, char** attn_ws,
+                            size_t* attn_bytes) {
+  const csa2_ragged& rg = a->rg;
+  const int64_t R = rg.num_rows;
+  const int64_t ld = round_up((size_t)(rg.max_entries > 0 ? rg.max_entries : 1), 64);
+  const int64_t blk_ld = round_up((size_t)(blocks_of(rg.max_entries) > 0 ? blocks_of(rg.max_entries) : 1), 64);
+  Carve c{base, 0};
+  float* s = a->scores ? nullptr : c.take<float>((size_t)R * ld);
+  if (scores) *scores = a->scores ? a->scores : s;
+  float* bs = c.take<float>((size_t)R * blk_ld);
+  if (blk_scores) *blk_scores = bs;
+  int32_t* kp = a->kept_blocks ? nullptr : c.take<int32_t>((size_t)R * (a->n_keep + 1));
+  if (kept) *kept = a->kept_blocks ? a->kept_blocks : kp;
+  int32_t* nk = a->n_kept ? nullptr : c.take<int32_t>((size_t)R);
+  if (n_kept) *n_kept = a->n_kept ? a->n_kept : nk;
+  int32_t* sl = a->sel_idx ? nullptr : c.take<int32_t>((size_t)R * a->k);
+  if (sel) *sel = a->sel_idx ? a->sel_idx : sl;
+  int32_t* ns = a->n_sel ? nullptr : c.take<int32_t>((size_t)R);
+  if (n_sel) *n_sel = a->n_sel ? a->n_sel : ns;
+  const size_t ab = attn_workspace_bytes(R, a->k);
+  char* aw = c.take<char>(ab);
+  if (attn_ws) *attn_ws = aw;
+  if (attn_bytes) *attn_bytes = ab;
+  return round_up(c.used, 256);
+}
+
+size_t csa2_decode_workspace_size(const csa2_decode_args* a) {
+  if (!a || a->rg.num_rows <= 0 || a->k < 1 || a->n_keep < 1) return 0;
+  return decode_layout(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (!a) return fail(CSA2_ERR_INVALID_ARG, "args is NULL");
+  RaggedDev g;
+  CHECK(check_ragged(&a->rg, g));
+  if (a->k < 1 || a->k > CSA2_K_MAX) return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d", CSA2_K_MAX);
+  if (a->n_keep < 1 || a->n_keep > CSA2_KEEP_MAX)
+    return fail(CSA2_ERR_UNSUPPORTED, "n_keep must be in 1..%d", CSA2_KEEP_MAX);
+  if (a->scan_mode != 0 && a->scan_mode != 1) return fail(CSA2_ERR_UNSUPPORTED, "scan_mode must be 0 or 1");
+  if (g.R == 0) return CSA2_OK;
+  CHECK(check_ptr(a->idx_k, 4, "idx_k"));
+  CHECK(check_ptr(a->blk_sum, 16, "blk_sum"));
+  CHECK(check_ptr(a->q_idx, 16, "q_idx"));
+  CHECK(check_ptr(a->w_idx, 4, "w_idx"));
+  if (a->scores && a->scores_ld < g.max_entries) return fail(CSA2_ERR_INVALID_ARG, "scores_ld < max_entries");
+  if ((a->kept_blocks == nullptr) != (a->n_kept == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "kept_blocks and n_kept must both be set or both be NULL");
+  if ((a->sel_idx == nullptr) != (a->n_sel == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "sel_idx and n_sel must both be set or both be NULL");
+  const size_t need = csa2_decode_workspace_size(a);
+  if (!ws || ws_bytes < need) return fail(CSA2_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu",
+                                          need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(CSA2_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  float *scores, *blk_scores;
+  int32_t *kept, *n_kept, *sel, *n_sel;
+  char* attn_ws;
+  size_t attn_bytes;
+  decode_layout(a, static_cast<char*>(ws), &scores, &blk_scores, &kept, &n_kept, &sel, &n_sel, &attn_ws, &attn_bytes);
+  const int64_t ld = a->scores ? a->scores_ld : (int64_t)round_up((size_t)(g.max_entries > 0 ? g.max_entries : 1), 64);
+  const int64_t blk_ld = (int64_t)round_up((size_t)(blocks_of(g.max_entries) > 0 ? blocks_of(g.max_entries) : 1), 64);
+
+  AttnArgs at{};
+  CHECK(attn_args(g, a->q, a->main_kv, sel, n_sel, a->k, a->swa, a->swa_scale, a->sm_scale, a->out, a->lse, attn_ws,
+                  attn_bytes, at));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  ScanArgs sa{};
+  sa.g = g;
+  sa.idx_k = a->idx_k;
+  sa.blk_sum = a->blk_sum;
+  sa.q_idx = a->q_idx;
+  sa.w = a->w_idx;
+  sa.scores = scores;
+  sa.ld = ld;
+  sa.blk_scores = blk_scores;
+  sa.blk_ld = blk_ld;
+
+  SelectArgs se{};
+  se.g = g;
+  se.blk_scores = blk_scores;
+  se.blk_ld = blk_ld;
+  se.n_keep = a->n_keep;
+  se.keep_newest = a->keep_newest ? 1 : 0;
+  se.kept = kept;
+  se.n_kept = n_kept;
+  se.kept_ld = a->n_keep + 1;
+  se.scores = scores;
+  se.ld = ld;
+  se.k = a->k;
+  se.sel = sel;
+  se.n_sel = n_sel;
+
+  auto mark = [&](int i) -> hipError_t {
+    return a->events ? hipEventRecord(static_cast<hipEvent_t>(a->events[i]), st) : hipSuccess;
+  };
+  LAUNCH(mark(0), "event record");
+  if (a->scan_mode == 0) {
+    // One launch scores every entry and every block summary; one launch selects.
+    LAUNCH(launch_scan(sa, a->rg.max_rows_per_request, true, true, st), "scan");
+    LAUNCH(mark(1), "event record");
+    LAUNCH(launch_select_fused(se, st), "select");
+  } else {
+    // Coarse stage first, then score only the kept blocks' entries.
+    LAUNCH(launch_scan(sa, a->rg.max_rows_per_request, false, true, st), "block scores");
+    LAUNCH(launch_block_select(se, st), "block select");
+    sa.kept = kept;
+    sa.n_kept = n_kept;
+    sa.kept_ld = a->n_keep + 1;
+    LAUNCH(launch_scan_kept(sa, st), "index scan (kept blocks)");
+    LAUNCH(mark(1), "event record");
+    LAUNCH(launch_topk(se, false, st), "top-k");
+  }
+  LAUNCH(mark(2), "event record");
+  LAUNCH(launch_attn_main(at, st), "sparse attention");
+  LAUNCH(mark(3), "event record");
+  LAUNCH(launch_attn_merge(at, st), "attention merge");
+  LAUNCH(mark(4), "event record");
+  return CSA2_OK;
+}
+
+int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales, int64_t n, float* out,
+                       void* stream) {
+  if (kind != CSA2_DQ_MAIN && kind != CSA2_DQ_IDX && kind != CSA2_DQ_SWA)
+    return fail(CSA2_ERR_INVALID_ARG, "unknown dequant kind %d", kind);
+  if (n < 0) return fail(CSA2_ERR_INVALID_ARG, "negative record count");
+  if (n == 0) return CSA2_OK;
+  CHECK(check_ptr(records, 4, "records"));
+  CHECK(check_ptr(out, 4, "out"));
+  if (kind == CSA2_DQ_SWA) CHECK(check_ptr(scales, 4, "scales"));
+  LAUNCH(launch_debug_dequant(kind, records, scales, n, out, reinterpret_cast<hipStream_t>(stream)), "dequant");
+  return CSA2_OK;
+}
+
+const char* csa2_status_string(int32_t status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported parameter";
+    case CSA2_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case CSA2_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* csa2_last_error(void) { return g_err; }
+
+int32_t csa2_version(void) { return CSA2_VERSION; }
+
+}  // extern "C"

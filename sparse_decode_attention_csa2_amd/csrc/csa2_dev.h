@@ -1,0 +1,150 @@
+// Device helpers shared by the gfx950 kernels of libcsa2: cache-format dequantisation
+// (FP4 E2M1 with E8M0 scales, FP8 E4M3FN), the bf16 MFMA, order-preserving score keys
+// and wave/workgroup scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa2.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace csa2 {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------
+// Dequantisation.  E2M1 values times an E8M0 power of two, and E4M3FN values, are
+// exact in bf16 (bf16 keeps fp32's exponent range), so every converted operand below is
+// the exact value of the stored code.
+// ---------------------------------------------------------------------------------
+
+// The scaled converts of gfx950 take the scale as an fp32 whose exponent field is the
+// E8M0 code (value 2^(u-127)).
+__device__ __forceinline__ float e8m0_operand(uint32_t u) { return __uint_as_float(u << 23); }
+
+// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16 x scale.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t codes, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 4 E4M3FN codes (one dword, element i in byte i) -> 4 bf16 (unscaled, exact).
+__device__ __forceinline__ bf16x4_t e4m3x4_to_bf16(uint32_t codes) {
+  const float one = 1.0f;
+  bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, one, false);
+  bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, one, true);
+  return bf16x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// fp32 -> bf16 bit pattern, round half to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Split 8 fp32 values into bf16 hi + lo parts (v ~= hi + lo to about 2^-17 relative),
+// packed as MFMA operands.  Integer packing only.
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t hw, lw;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t h0 = bf16_bits_rne(v[2 * q]), h1 = bf16_bits_rne(v[2 * q + 1]);
+    const float r0 = v[2 * q] - __uint_as_float(h0 << 16);
+    const float r1 = v[2 * q + 1] - __uint_as_float(h1 << 16);
+    hw[q] = h0 | (h1 << 16);
+    lw[q] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, hw);
+  lo = __builtin_bit_cast(bf16x8_t, lw);
+}
+
+// Widen 8 bf16 to fp32 through the packed 32-bit words (integer shifts only).
+__device__ __forceinline__ void bf16x8_words_to_f32(bf16x8_t x, float (&v)[8]) {
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, x);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x4_t as_bf16x4(u32x2_t v) { return __builtin_bit_cast(bf16x4_t, v); }
+
+// 16-byte load from an address that is only 4-byte aligned (68-B records); gfx950
+// global loads accept it.
+__device__ __forceinline__ u32x4_t load16_a4(const uint8_t* p) {
+  typedef uint32_t u32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+  return *reinterpret_cast<const u32x4a4_t*>(p);
+}
+__device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+// ---------------------------------------------------------------------------------
+// MFMA: D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%16][8*(l/16) + j] and B[8*(l/16) + j][l%16] (j < 8), and receives
+// D[4*(l/16) + i][l%16] (i < 4).
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------
+// Selection keys: larger score -> larger unsigned key; +0 and -0 map to one key.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    T o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a workgroup of NT threads; `tmp` is LDS of NT/64 + 1 entries.
+// Also returns the total.  Contains two barriers.
+template <int NT, typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T* tmp, T& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  T incl = wave_incl_scan(v);
+  if (lane == kWave - 1) tmp[wave] = incl;
+  __syncthreads();
+  T before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    T x = tmp[w];
+    if (w < wave) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+}  // namespace csa2

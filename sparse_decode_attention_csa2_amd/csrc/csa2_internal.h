@@ -1,0 +1,130 @@
+// Internal interfaces between libcsa2's host entry points and its kernels.
+#pragma once
+
+#include "csa2_dev.h"
+
+namespace csa2 {
+
+// The ragged descriptor as the kernels see it: device offset arrays plus host maxima
+// used both for grid sizing and to clamp every device-provided offset.
+struct RaggedDev {
+  const int64_t* entry_off;
+  const int64_t* block_off;
+  const int32_t* row_off;
+  const int32_t* row_req;
+  const int64_t* row_swa_start;
+  const int32_t* row_swa_len;
+  int64_t max_entries;
+  int64_t total_entries;
+  int64_t total_blocks;
+  int64_t swa_tokens;
+  int32_t B;
+  int32_t R;
+};
+
+// Entries of request b, clamped to the pool and to max_entries.
+__device__ __forceinline__ void req_entries(const RaggedDev& g, int b, int64_t& e0, int64_t& n) {
+  const int64_t a = clamp64(g.entry_off[b], 0, g.total_entries);
+  const int64_t z = clamp64(g.entry_off[b + 1], a, g.total_entries);
+  e0 = a;
+  n = (z - a) < g.max_entries ? (z - a) : g.max_entries;
+}
+
+// First summary of request b and how many of its ceil(n/64) summaries the pool holds.
+__device__ __forceinline__ void req_blocks(const RaggedDev& g, int b, int64_t n, int64_t& bl0, int64_t& nb_avail) {
+  bl0 = clamp64(g.block_off[b], 0, g.total_blocks);
+  const int64_t nb = (n + CSA2_BLOCK - 1) / CSA2_BLOCK;
+  nb_avail = (g.total_blocks - bl0) < nb ? (g.total_blocks - bl0) : nb;
+}
+
+// Rows of request b, clamped to [0, R) and to at most `cap` rows.
+__device__ __forceinline__ void req_rows(const RaggedDev& g, int b, int cap, int& r0, int& r1) {
+  int a = g.row_off[b], z = g.row_off[b + 1];
+  a = a < 0 ? 0 : (a > g.R ? g.R : a);
+  z = z < a ? a : (z > g.R ? g.R : z);
+  if (z - a > cap) z = a + cap;
+  r0 = a;
+  r1 = z;
+}
+
+__device__ __forceinline__ int row_request(const RaggedDev& g, int r) {
+  int b = g.row_req[r];
+  return b < 0 ? 0 : (b >= g.B ? g.B - 1 : b);
+}
+
+// --------------------------------------------------------------------------------
+// Launchers (each returns the launch's hipError_t).
+// --------------------------------------------------------------------------------
+
+struct ScanArgs {
+  RaggedDev g;
+  const uint8_t* idx_k;
+  const uint16_t* blk_sum;
+  const uint16_t* q_idx;
+  const float* w;
+  float* scores;          // [R][ld]   (entry part)
+  int64_t ld;
+  float* blk_scores;      // [R][blk_ld] (block part)
+  int64_t blk_ld;
+  int32_t entry_tiles;    // workgroups of the entry part (grid.x before the block part)
+  int32_t block_tiles;    // workgroups of the block part
+  const int32_t* kept;    // candidate-only scan: [R][kept_ld]
+  const int32_t* n_kept;
+  int32_t kept_ld;
+};
+
+hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool blocks, hipStream_t st);
+hipError_t launch_scan_kept(ScanArgs a, hipStream_t st);
+
+struct SelectArgs {
+  RaggedDev g;
+  const float* blk_scores;   // [R][blk_ld]
+  int64_t blk_ld;
+  int32_t n_keep;
+  int32_t keep_newest;
+  int32_t* kept;             // [R][kept_ld]
+  int32_t* n_kept;           // [R]
+  int32_t kept_ld;
+  const float* scores;       // [R][ld]
+  int64_t ld;
+  int32_t k;
+  int32_t* sel;              // [R][k]
+  int32_t* n_sel;            // [R]
+  float* sel_score;          // nullable [R][k]
+};
+
+hipError_t launch_block_select(SelectArgs a, hipStream_t st);
+hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st);
+hipError_t launch_select_fused(SelectArgs a, hipStream_t st);
+
+struct AttnArgs {
+  RaggedDev g;
+  const uint16_t* q;
+  const uint8_t* main_kv;
+  const int32_t* sel;
+  const int32_t* n_sel;
+  int32_t sel_ld;
+  const uint8_t* swa;
+  const float* swa_scale;
+  float sm_scale_log2;       // sm_scale * log2(e)
+  int32_t tiles_per_split;
+  int32_t splits;
+  float* opart;              // [R][splits][64][512]
+  float* mpart;              // [R][splits][64]
+  float* lpart;              // [R][splits][64]
+  float* out;                // [R][64][512]
+  float* lse;                // [R][64]
+};
+
+constexpr int kAttnTile = 32;  // keys per tile
+
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tiles_per_split, int32_t& splits);
+size_t attn_workspace_bytes(int64_t R, int32_t sel_ld);
+hipError_t launch_attn(AttnArgs a, hipStream_t st);
+hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
+
+hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
+                                hipStream_t st);
+
+}  // namespace csa2

@@ -224,13 +224,14 @@ def _gen_main_chunk(seed, b, c, n_total):
 
 def make_workload(name: str, seed: int, n_entries: list, rows_per_req: list | int = 1,
                   n_needles: int = 16, swa_len: int | list = SWA_LEN, n_tokens: list | None = None,
-                  workers: int | None = None) -> Workload:
+                  workers: int | None = None, scan_only: bool = False) -> Workload:
     """Build a workload with request b holding ``n_entries[b]`` global entries.
 
     Request b has ``rows_per_req[b]`` query rows; its window buffer holds
     ``swa_len + rows - 1`` tokens and row j of the request sees tokens j .. j+swa_len-1
     (the window slides causally with the row's position).  ``swa_len`` may be a list
-    (one per request, 0..128).  Needles: ``n_needles`` distinct positions per request
+    (one per request, 0..128).  ``scan_only`` leaves the main-KV pool zero (for
+    measuring the indexer scan alone).  Needles: ``n_needles`` distinct positions per request
     whose indexer key is 3x the head-mean of the request's first row's indexer query.
     """
     B = len(n_entries)
@@ -294,10 +295,11 @@ def make_workload(name: str, seed: int, n_entries: list, rows_per_req: list | in
     def run(job):
         b, c, n, pos, nkey = job
         ik, summ = _gen_idx_chunk(seed, b, c, n, pos, nkey)
-        mk = _gen_main_chunk(seed, b, c, n)
         e0 = int(entry_off[b]) + c * CHUNK
         idx_k[e0:e0 + ik.shape[0]] = ik
-        main_kv[e0:e0 + mk.shape[0]] = mk
+        if not scan_only:
+            mk = _gen_main_chunk(seed, b, c, n)
+            main_kv[e0:e0 + mk.shape[0]] = mk
         b0 = int(block_off[b]) + c * (CHUNK // SUMMARY_BLOCK)
         blk_sum[b0:b0 + summ.shape[0]] = summ
 

@@ -1,0 +1,134 @@
+"""End-to-end parity of csa2_decode against the oracle on the five decode workloads and
+on edge cases (needs an MI355X)."""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import parity
+from synth import make_config, make_workload
+from synth.device import upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    import sparse_decode_attention_csa2_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libcsa2.so missing: the HIP path must be built before GPU tests")
+    m.load_library()
+    return m
+
+
+def run_decode(csa2, wl, **kw):
+    dw = upload(wl)
+    d = csa2.Decoder(*dw.decode_inputs(), k=kw.pop("k", wl.k), n_keep=kw.pop("n_keep", wl.n_keep),
+                     keep_newest=bool(kw.pop("keep_newest", wl.keep_newest)), sm_scale=wl.sm_scale, **kw)
+    d.run()
+    torch.cuda.synchronize()
+    return dict(out=d.out.cpu().numpy(), lse=d.lse.cpu().numpy(), sel=d.sel_idx.cpu().numpy(),
+                n_sel=d.n_sel.cpu().numpy(), kept=d.kept.cpu().numpy(), n_kept=d.n_kept.cpu().numpy(),
+                scores=d.scores.cpu().numpy())
+
+
+def judge(wl, got, refs, rows=None, k=None, n_keep=None):
+    rows = list(range(wl.num_rows)) if rows is None else rows
+    reports = []
+    for r, ref in zip(rows, refs):
+        rep = parity.check_row(wl, r, ref, got["kept"][r, :got["n_kept"][r]], got["sel"][r, :got["n_sel"][r]],
+                               got["out"][r], got["lse"][r], k=k, n_keep=n_keep)
+        reports.append(rep)
+    bad = [rp for rp in reports if not rp["ok"]]
+    worst = max((rp["attn_rel_own"] for rp in reports), default=0.0)
+    _log(f"  rows {len(reports)}: sets equal {sum(rp['set_equal'] for rp in reports)}, "
+         f"kept equal {sum(rp.get('kept_equal', True) for rp in reports)}, worst attn rel {worst:.2e}")
+    assert not bad, "; ".join(f"row {rp['row']}: {' | '.join(rp['msgs'])}" for rp in bad[:5])
+    return reports
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_decode_config_matches_oracle(csa2, cfg):
+    t0 = time.time()
+    wl = make_config(cfg)
+    _log(f"config {cfg} ({wl.name}): {wl.num_requests} requests, {wl.num_rows} rows, "
+         f"{wl.total_entries} entries (generated in {time.time() - t0:.1f}s)")
+    got = run_decode(csa2, wl)
+    _log(f"  decode done; oracle ...")
+    refs = oracle.decode(wl)
+    # Index scores (diagnostic bound: fp32 vs fp64 within 1e-5 of the mean score).
+    for b in range(wl.num_requests):
+        r0 = int(wl.row_off[b])
+        n = wl.n_entries(b)
+        ref = refs[r0]["scores"]
+        err = np.abs(got["scores"][r0, :n] - ref).max() / np.abs(ref).mean()
+        assert err <= 1e-5, f"request {b}: score error {err:.3g}"
+    judge(wl, got, refs)
+    _log(f"  config {cfg} ok in {time.time() - t0:.1f}s")
+
+
+def test_decode_candidate_only_scan_matches_full_scan(csa2):
+    wl = make_config(3)
+    full = run_decode(csa2, wl)
+    cand = run_decode(csa2, wl, scan_mode=1)
+    assert np.array_equal(full["sel"], cand["sel"]) and np.array_equal(full["n_sel"], cand["n_sel"])
+    assert np.array_equal(full["kept"], cand["kept"])
+    assert np.array_equal(full["out"], cand["out"]) and np.array_equal(full["lse"], cand["lse"])
+
+
+def test_decode_is_deterministic(csa2):
+    wl = make_config(2)
+    a = run_decode(csa2, wl)
+    b = run_decode(csa2, wl)
+    for key in ("out", "lse", "sel", "kept", "scores"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_decode_edge_workloads(csa2):
+    # Empty request, single entry, partial blocks, nb <= 64 (coarse stage keeps all),
+    # nb just above 64, N < k, windows of 0..128 tokens, several rows per request.
+    lens = [0, 1, 63, 64, 65, 511, 513, 64 * 64, 64 * 64 + 1, 64 * 65, 64 * 65 + 63, 20000]
+    swa = [0, 1, 128, 5, 0, 128, 77, 128, 128, 1, 128, 128]
+    rows = [1, 1, 2, 1, 1, 3, 1, 1, 6, 1, 1, 2]
+    wl = make_workload("edge", 99, lens, rows_per_req=rows, n_needles=4, swa_len=swa)
+    _log(f"edge workload: {len(lens)} requests, {wl.num_rows} rows")
+    got = run_decode(csa2, wl)
+    refs = oracle.decode(wl)
+    judge(wl, got, refs)
+    r_empty = 0
+    assert got["n_sel"][r_empty] == 0 and np.all(np.isneginf(got["lse"][r_empty]))
+    assert np.all(got["out"][r_empty] == 0)
+
+
+@pytest.mark.parametrize("k,n_keep,newest", [(100, 10, True), (2048, 128, True), (512, 64, False), (1, 1, True)])
+def test_decode_parameters(csa2, k, n_keep, newest):
+    wl = make_workload("params", 7 + k, [64 * 300 + 3, 4096, 64 * 129], rows_per_req=[1, 2, 1], n_needles=16)
+    _log(f"decode k {k} n_keep {n_keep} newest {newest}")
+    got = run_decode(csa2, wl, k=k, n_keep=n_keep, keep_newest=newest)
+    refs = oracle.decode(wl, k=k, n_keep=n_keep, keep_newest=int(newest))
+    judge(wl, got, refs, k=k, n_keep=n_keep)
+
+
+def test_decode_keep_all_is_dense_attention(csa2):
+    # k >= N and n_keep >= nb: every entry is selected and the result is dense attention
+    # over all entries plus the window.
+    wl = make_workload("dense", 17, [2000, 64 * 100], rows_per_req=[2, 1], n_needles=0)
+    got = run_decode(csa2, wl, k=2048, n_keep=128)
+    for r in range(wl.num_rows):
+        b = int(wl.row_req[r])
+        n = wl.n_entries(b)
+        if n <= 2048:
+            assert got["sel"][r, :got["n_sel"][r]].tolist() == list(range(n))
+            ro, rl = oracle.joint_attention(oracle.bf16_value(wl.q[r]), oracle.row_keys(wl, r, np.arange(n)),
+                                            wl.sm_scale)
+            rel, dl = parity.attn_error(got["out"][r], got["lse"][r], ro, rl)
+            assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS
