@@ -110,16 +110,48 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no LDS round
+// trips): row_shr 1/2/4/8 scans each row of 16 lanes, then row_bcast15 and row_bcast31
+// carry row totals into the following rows.  Lanes a move has no source for add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Wave-wide max / min of 32-bit unsigned values on DPP moves; lane 63 ends with the
+// result, which readlane makes uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return ~wave_max_u32(~x);
+}
+
 template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    T o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
+__device__ __forceinline__ T wave_incl_scan(T v);
+
+template <>
+__device__ __forceinline__ uint32_t wave_incl_scan<uint32_t>(uint32_t v) { return wave_incl_scan_u32(v); }
+
+template <>
+__device__ __forceinline__ int wave_incl_scan<int>(int v) { return (int)wave_incl_scan_u32((uint32_t)v); }
+
+// 64-bit values as two 32-bit halves (each half's sum must stay below 2^32).
+template <>
+__device__ __forceinline__ uint64_t wave_incl_scan<uint64_t>(uint64_t v) {
+  const uint32_t lo = wave_incl_scan_u32((uint32_t)v), hi = wave_incl_scan_u32((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Exclusive prefix sum over a workgroup of NT threads; `tmp` is LDS of NT/64 + 1 entries.
