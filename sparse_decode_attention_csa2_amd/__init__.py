@@ -218,8 +218,13 @@ def topk(rg: Ragged, scores, kept=None, n_kept=None, k: int = 512, with_scores: 
     return sel, n_sel, ss
 
 
-def sparse_attn(rg: Ragged, q, main_kv, sel_idx, n_sel, swa, swa_scale, sm_scale: float = 1.0 / math.sqrt(D)):
-    """(out fp32 [R][64][512], lse fp32 [R][64])."""
+def sparse_attn_workspace_size(rg: Ragged, sel_ld: int) -> int:
+    return int(load_library().csa2_sparse_attn_workspace_size(ctypes.byref(rg.c()), sel_ld))
+
+
+def sparse_attn(rg: Ragged, q, main_kv, sel_idx, n_sel, swa, swa_scale, sm_scale: float = 1.0 / math.sqrt(D),
+                out=None, lse=None, ws=None):
+    """(out fp32 [R][64][512], lse fp32 [R][64]); out/lse/ws may be caller-provided."""
     lib = load_library()
     _dev(q, _BF16, "q")
     _dev(main_kv, (torch.uint8,), "main_kv")
@@ -228,12 +233,15 @@ def sparse_attn(rg: Ragged, q, main_kv, sel_idx, n_sel, swa, swa_scale, sm_scale
     _dev(swa, (torch.uint8,), "swa")
     _dev(swa_scale, (torch.float32,), "swa_scale")
     R = rg.num_rows
-    out = _empty((R, HEADS, D), torch.float32, q)
-    lse = _empty((R, HEADS), torch.float32, q)
+    out = _empty((R, HEADS, D), torch.float32, q) if out is None else _dev(out, (torch.float32,), "out")
+    lse = _empty((R, HEADS), torch.float32, q) if lse is None else _dev(lse, (torch.float32,), "lse")
     c = rg.c()
     sel_ld = sel_idx.shape[-1]
     nws = lib.csa2_sparse_attn_workspace_size(ctypes.byref(c), sel_ld)
-    ws = _empty((max(nws, 1),), torch.uint8, q)
+    if ws is None:
+        ws = _empty((max(nws, 1),), torch.uint8, q)
+    elif ws.numel() < nws:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {nws} needed")
     _check(lib.csa2_sparse_attn(ctypes.byref(c), _ptr(q), _ptr(main_kv), _ptr(sel_idx), _ptr(n_sel), sel_ld,
                                 _ptr(swa), _ptr(swa_scale), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), nws,
                                 _stream()))
@@ -291,6 +299,29 @@ class Decoder:
         self._args.events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
         _check(self._lib.csa2_decode(ctypes.byref(self._args), _ptr(self.ws), self.ws_bytes,
                                      _stream() if stream is None else stream))
+
+
+def capture_calls(fns) -> "torch.cuda.CUDAGraph":
+    """Capture the launches made by calling each of ``fns`` (in order) into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    return g
+
+
+def capture_graph(decoders, events=None) -> "torch.cuda.CUDAGraph":
+    """Capture one csa2_decode launch chain per decoder (in order) into a HIP graph.
+
+    ``events`` (optional) holds one DECODE_EVENTS handle array per decoder; the event
+    records are captured with the kernels.  The decoders must have run eagerly once.
+    Replaying the graph re-enqueues every captured step on the current stream.
+    """
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i, d in enumerate(decoders):
+            d.run(events=None if events is None else events[i])
+    return g
 
 
 def decode(rg: Ragged, idx_k, main_kv, blk_sum, swa, swa_scale, q, q_idx, w_idx, **kw) -> Decoder:

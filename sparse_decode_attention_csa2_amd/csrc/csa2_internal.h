@@ -66,8 +66,8 @@ struct ScanArgs {
   int64_t ld;
   float* blk_scores;      // [R][blk_ld] (block part)
   int64_t blk_ld;
-  int32_t entry_tiles;    // workgroups of the entry part (grid.x before the block part)
-  int32_t block_tiles;    // workgroups of the block part
+  int32_t entry_tiles;    // workgroups of the entry part (grid.x after the block part)
+  int32_t block_tiles;    // workgroups of the block part (first in grid.x)
   const int32_t* kept;    // candidate-only scan: [R][kept_ld]
   const int32_t* n_kept;
   int32_t kept_ld;

@@ -67,7 +67,9 @@ __device__ __forceinline__ void score_group(const bf16x8_t (&kb)[4], const bf16x
   }
 }
 
-template <int MAXPAIRS>
+// PARTS: 1 = entries only, 2 = block summaries only, 3 = both in one launch (distinct
+// instantiations keep the variants apart in kernel traces).
+template <int MAXPAIRS, int PARTS>
 __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   const int b = blockIdx.y;
   int64_t e0, n;
@@ -78,8 +80,10 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   const int npairs = (r1 - r0 + 1) >> 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, g = lane >> 4;
 
-  if ((int)blockIdx.x < a.entry_tiles) {
-    const int64_t base = (int64_t)blockIdx.x * kTile + wave * (kGroups * 16);
+  // Block-summary tiles come first in the grid so that they start early and do not
+  // trail the (many more) entry tiles.
+  if ((int)blockIdx.x >= a.block_tiles) {
+    const int64_t base = (int64_t)(blockIdx.x - a.block_tiles) * kTile + wave * (kGroups * 16);
     if (base >= n) return;
     // Issue every load of the wave's tile before any conversion.
     u32x4_t kc[kGroups];
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   } else {
     int64_t bl0, nb;
     req_blocks(a.g, b, n, bl0, nb);
-    const int64_t base = (int64_t)(blockIdx.x - a.entry_tiles) * kTile + wave * (kGroups * 16);
+    const int64_t base = (int64_t)blockIdx.x * kTile + wave * (kGroups * 16);
     if (base >= nb) return;
     bf16x8_t qa[MAXPAIRS][4];
     float wv[MAXPAIRS][4];
@@ -164,21 +168,31 @@ __global__ __launch_bounds__(64) void k_scan_kept(ScanArgs a) {
 
 }  // namespace
 
+template <int PARTS>
+static void launch_scan_parts(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
+  if (max_rows_per_req <= 2)
+    k_scan<1, PARTS><<<grid, dim3(256), 0, st>>>(a);
+  else if (max_rows_per_req <= 4)
+    k_scan<2, PARTS><<<grid, dim3(256), 0, st>>>(a);
+  else if (max_rows_per_req <= 8)
+    k_scan<4, PARTS><<<grid, dim3(256), 0, st>>>(a);
+  else
+    k_scan<8, PARTS><<<grid, dim3(256), 0, st>>>(a);
+}
+
 hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool blocks, hipStream_t st) {
   const int64_t max_nb = (a.g.max_entries + CSA2_BLOCK - 1) / CSA2_BLOCK;
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + kTile - 1) / kTile) : 0;
   a.block_tiles = blocks ? (int32_t)((max_nb + kTile - 1) / kTile) : 0;
   const int gx = a.entry_tiles + a.block_tiles;
   if (gx == 0 || a.g.B == 0 || a.g.R == 0) return hipSuccess;
-  dim3 grid(gx, a.g.B), block(256);
-  if (max_rows_per_req <= 2)
-    k_scan<1><<<grid, block, 0, st>>>(a);
-  else if (max_rows_per_req <= 4)
-    k_scan<2><<<grid, block, 0, st>>>(a);
-  else if (max_rows_per_req <= 8)
-    k_scan<4><<<grid, block, 0, st>>>(a);
+  const dim3 grid(gx, a.g.B);
+  if (entries && blocks)
+    launch_scan_parts<3>(a, max_rows_per_req, grid, st);
+  else if (entries)
+    launch_scan_parts<1>(a, max_rows_per_req, grid, st);
   else
-    k_scan<8><<<grid, block, 0, st>>>(a);
+    launch_scan_parts<2>(a, max_rows_per_req, grid, st);
   return hipGetLastError();
 }
 
