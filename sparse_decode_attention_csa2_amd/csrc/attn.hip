@@ -8,14 +8,16 @@
 //   z_i = sm_scale * q_h . x_i,  out_h = sum_i softmax(z)_i x_i,  lse_h = log sum_i e^z_i.
 //
 // Kernel structure.  A workgroup (4 waves) takes a range of 32-key tiles of one row.
-// Per tile, the 256 threads gather the keys' records and dequantise them (exactly) to
-// bf16 in LDS twice: key-major Kl[key][dim] for S^T = K Q^T and dim-major Vt[dim][key]
-// for O^T = V^T P^T.  Window tokens enter as their exact E4M3 values; their fp32 scale
-// multiplies the logits and the probabilities instead.  Wave w owns heads 16w..16w+15
-// (query fragments stay in registers for all tiles); both products run on bf16 16x16x32
-// MFMAs with fp32 accumulation, with an online softmax between them.  Workgroups of one
-// row write (unnormalised O, running max, running sum) partials that a second kernel
-// merges by log-sum-exp; with a single split the kernel writes the result directly.
+// Each thread owns two keys x 32 dims of a tile: it loads their records one tile ahead
+// (the loads of tile j+1 are in flight while tile j computes) and dequantises them
+// exactly to bf16 into LDS twice: key-major Kl[key][dim] for S^T = K Q^T and dim-major
+// Vt[dim][key] (the two keys packed per 32-bit word) for O^T = V^T P^T.  Window tokens
+// enter as their exact E4M3 values; their fp32 scale multiplies the logits and the
+// probabilities instead.  Wave w owns heads 16w..16w+15 (query fragments stay in
+// registers for all tiles); both products run on bf16 16x16x32 MFMAs with fp32
+// accumulation, with an online softmax between them.  Workgroups of one row write
+// (unnormalised O, running max, running sum) partials that a second kernel merges by
+// log-sum-exp; with a single split the kernel writes the result directly.
 #include <math.h>
 
 #include "csa2_internal.h"
@@ -23,11 +25,9 @@
 namespace csa2 {
 namespace {
 
-constexpr int TK = kAttnTile;   // 32 keys per tile
 constexpr int KLS = 520;        // Kl row stride in bf16 (512 + 8: 16-B aligned rows, spread banks)
-constexpr int VTS = 36;         // Vt row stride in bf16 (32 + 4)
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSplitKeys = CSA2_K_MAX + CSA2_SWA_MAX;   // positions of one split staged in LDS
 
 struct RowKeys {
   int64_t e0, n;     // request's first pool entry and entry count
@@ -56,15 +56,49 @@ __device__ __forceinline__ RowKeys row_keys(const AttnArgs& a, int r) {
   return k;
 }
 
-__device__ __forceinline__ void st_b128(uint16_t* p, bf16x8_t v) {
-  *reinterpret_cast<u32x4_t*>(p) = __builtin_bit_cast(u32x4_t, v);
+// One key's raw record slice as loaded by its thread (dims 32ch .. 32ch+31).
+struct KeyRegs {
+  u32x4_t c0, c1;     // main: c0 = 16 code bytes; window: c0, c1 = 32 E4M3 bytes
+  uint32_t sc;        // main: two E8M0 bytes (blocks 2ch, 2ch+1); window: fp32 scale bits
+  int kind;           // 0 empty, 1 main entry, 2 window token
+};
+
+// Exact bf16 values of a key's 32 dims as 16 packed words (element 2q in the low half).
+__device__ __forceinline__ void convert_key(const KeyRegs& k, uint32_t (&w)[16]) {
+  if (k.kind == 1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4_t x = __builtin_bit_cast(u32x4_t, fp4x8_to_bf16(k.c0[d], e8m0_operand((k.sc >> (8 * (d >> 1))) & 255u)));
+      w[4 * d] = x[0];
+      w[4 * d + 1] = x[1];
+      w[4 * d + 2] = x[2];
+      w[4 * d + 3] = x[3];
+    }
+  } else if (k.kind == 2) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t c = d < 4 ? k.c0[d] : k.c1[d - 4];
+      const u32x2_t x = __builtin_bit_cast(u32x2_t, e4m3x4_to_bf16(c));
+      w[2 * d] = x[0];
+      w[2 * d + 1] = x[1];
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) w[d] = 0u;
+  }
 }
 
+// KB = 32-key groups per tile (tile = 32 KB keys).
+template <int KB>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  constexpr int TK = 32 * KB;
+  constexpr int VTS = TK + 4;          // Vt row stride in bf16
+  constexpr int NB = 2 * KB;           // 16-key blocks per tile
   __shared__ __align__(16) uint16_t Kl[TK * KLS];
   __shared__ __align__(16) uint16_t Vt[CSA2_D * VTS];
   __shared__ float ksc[TK];
   __shared__ int kval[TK];
+  __shared__ int32_t spos[kMaxSplitKeys];
 
   const int r = blockIdx.y, split = blockIdx.x;
   const RowKeys rk = row_keys(a, r);
@@ -83,6 +117,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   if (k_begin >= n_keys) return;
   const int k_end = min(n_keys, k_begin + a.tiles_per_split * TK);
 
+  // Stage the split's selected positions in LDS (one round trip for all tiles).
+  {
+    const int m_end = min(k_end, rk.n_main);
+    for (int i = k_begin + tid; i < m_end; i += 256) spos[i - k_begin] = a.sel[(int64_t)r * a.sel_ld + i];
+  }
   // Query fragments (B operand of S^T = K Q^T): lane holds q[h][32*st + 8g + j].
   bf16x8_t qb[16];
   {
@@ -90,102 +129,119 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int st = 0; st < 16; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
   }
+  __syncthreads();
 
   f32x4_t o[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kk = tid & (TK - 1);   // dequant role: key kk of the tile ...
-  const int ch = tid >> 5;         // ... dims 64ch .. 64ch+63
-
-  for (int kt = k_begin; kt < k_end; kt += TK) {
-    __syncthreads();   // the previous tile's LDS reads are done
-    {
-      const int i = kt + kk;
-      bf16x8_t x[8];
-      bool valid = false;
-      float scale = 0.f;
+  // Dequant role: keys 32u + 2kp + e (u < KB, e < 2) of a tile, dims 32ch .. 32ch+31.
+  const int kp = tid & 15, ch = tid >> 4;
+  const int32_t* sp = spos - k_begin;   // position of key i is sp[i] (i in the split)
+  KeyRegs kr[2 * KB];
+  auto load_keys = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < 2 * KB; ++u) {
+      const int i = kt + 32 * (u >> 1) + 2 * kp + (u & 1);
+      KeyRegs k;
+      k.kind = 0;
+      k.c0 = u32x4_t{0u, 0u, 0u, 0u};
+      k.c1 = k.c0;
+      k.sc = 0u;
       if (i < k_end) {
         if (i < rk.n_main) {
-          const int64_t pos = a.sel[(int64_t)r * a.sel_ld + i];
+          const int64_t pos = sp[i];
           if (pos >= 0 && pos < rk.n) {
             const uint8_t* rec = a.main_kv + (rk.e0 + pos) * CSA2_MAIN_BYTES;
-            const u32x4_t c0 = load16(rec + 32 * ch);
-            const u32x4_t c1 = load16(rec + 32 * ch + 16);
-            const uint32_t s4 = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * ch);
-            const uint32_t wd[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-#pragma unroll
-            for (int w = 0; w < 8; ++w) x[w] = fp4x8_to_bf16(wd[w], e8m0_operand((s4 >> (8 * (w >> 1))) & 255u));
-            valid = true;
-            scale = 1.f;
+            k.c0 = load16(rec + 16 * ch);
+            k.sc = *reinterpret_cast<const uint16_t*>(rec + 256 + 2 * ch);
+            k.kind = 1;
           }
         } else {
           const int64_t tok = rk.s0 + (i - rk.n_main);
-          const uint8_t* rec = a.swa + tok * CSA2_D + 64 * ch;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const u32x4_t c = load16(rec + 16 * u);
-            const bf16x4_t lo0 = e4m3x4_to_bf16(c[0]), hi0 = e4m3x4_to_bf16(c[1]);
-            const bf16x4_t lo1 = e4m3x4_to_bf16(c[2]), hi1 = e4m3x4_to_bf16(c[3]);
-            x[2 * u] = bf16x8_t{lo0[0], lo0[1], lo0[2], lo0[3], hi0[0], hi0[1], hi0[2], hi0[3]};
-            x[2 * u + 1] = bf16x8_t{lo1[0], lo1[1], lo1[2], lo1[3], hi1[0], hi1[1], hi1[2], hi1[3]};
-          }
-          valid = true;
-          scale = a.swa_scale[tok];
+          const uint8_t* rec = a.swa + tok * CSA2_D + 32 * ch;
+          k.c0 = load16(rec);
+          k.c1 = load16(rec + 16);
+          k.sc = __float_as_uint(a.swa_scale[tok]);
+          k.kind = 2;
         }
       }
-      if (!valid) {
+      kr[u] = k;
+    }
+  };
+  load_keys(k_begin);
+
+  for (int kt = k_begin; kt < k_end; kt += TK) {
+    // Convert this tile's records (already in registers) into LDS: key-major Kl and
+    // dim-major Vt (two keys packed per 32-bit word).
 #pragma unroll
-        for (int w = 0; w < 8; ++w) x[w] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    for (int u = 0; u < KB; ++u) {
+      uint32_t w0[16], w1[16];
+      convert_key(kr[2 * u], w0);
+      convert_key(kr[2 * u + 1], w1);
+      const int key0 = 32 * u + 2 * kp;
+      uint16_t* k0 = Kl + key0 * KLS + 32 * ch;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<u32x4_t*>(k0 + 8 * q) = u32x4_t{w0[4 * q], w0[4 * q + 1], w0[4 * q + 2], w0[4 * q + 3]};
+        *reinterpret_cast<u32x4_t*>(k0 + KLS + 8 * q) = u32x4_t{w1[4 * q], w1[4 * q + 1], w1[4 * q + 2], w1[4 * q + 3]};
       }
-      uint16_t* kr = Kl + kk * KLS + 64 * ch;
+      uint32_t* vt = reinterpret_cast<uint32_t*>(Vt + (32 * ch) * VTS + key0);
 #pragma unroll
-      for (int w = 0; w < 8; ++w) st_b128(kr + 8 * w, x[w]);
-      // Transposed copy, one 16-bit element at a time.  The halves are split from the
-      // 32-bit words with integer shifts: element extraction from a bf16 vector into a
-      // 16-bit store is mis-selected by this compiler (every store took the low half of
-      // the first word).
-      uint16_t* vc = Vt + (64 * ch) * VTS + kk;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const u32x4_t xw = __builtin_bit_cast(u32x4_t, x[w]);
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          vc[(8 * w + 2 * q2) * VTS] = (uint16_t)(xw[q2] & 0xFFFFu);
-          vc[(8 * w + 2 * q2 + 1) * VTS] = (uint16_t)(xw[q2] >> 16);
-        }
+      for (int q = 0; q < 16; ++q) {
+        vt[(2 * q) * (VTS / 2)] = (w0[q] & 0xFFFFu) | (w1[q] << 16);
+        vt[(2 * q + 1) * (VTS / 2)] = (w0[q] >> 16) | (w1[q] & 0xFFFF0000u);
       }
       if (ch == 0) {
-        ksc[kk] = valid ? scale : 0.f;
-        kval[kk] = valid ? 1 : 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const KeyRegs& k = kr[2 * u + e];
+          ksc[key0 + e] = k.kind == 2 ? __uint_as_float(k.sc) : (k.kind == 1 ? 1.f : 0.f);
+          kval[key0 + e] = k.kind != 0;
+        }
       }
     }
     __syncthreads();
+    // Prefetch the next tile's records while this one computes.
+    if (kt + TK < k_end) load_keys(kt + TK);
 
-    // S^T[key][head] for the tile's 32 keys (two 16-key M tiles) and this wave's 16 heads.
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // S^T[key][head] for the tile's keys (16-key blocks b) and this wave's 16 heads.
+    // With one 32-key group the even and odd K steps use separate accumulators so that
+    // four MFMA chains are in flight.
+    constexpr int PAR = KB == 1 ? 2 : 1;
+    f32x4_t s[NB][PAR];
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + ln * KLS + 32 * st + 8 * g));
-      const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 + ln) * KLS + 32 * st + 8 * g));
-      s0 = mfma16x16x32(a0, qb[st], s0);
-      s1 = mfma16x16x32(a1, qb[st], s1);
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int p = 0; p < PAR; ++p) s[b][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 16; st += PAR) {
+#pragma unroll
+      for (int p = 0; p < PAR; ++p) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8_t ak = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 32 * (st + p) + 8 * g));
+          s[b][p] = mfma16x16x32(ak, qb[st + p], s[b][p]);
+        }
+      }
     }
-    // Lane holds keys 4g+i (s0) and 16+4g+i (s1) for head h.
-    float z[8];
-    float sc[8];
+    // Lane holds keys 16b + 4g + i for head h.
+    float z[4 * NB], sc[4 * NB];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-      const float s = (j < 4) ? s0[j] : s1[j - 4];
-      const bool ok = (kt + key < k_end) && kval[key];
-      sc[j] = ksc[key];
-      z[j] = ok ? s * sc[j] * a.sm_scale_log2 : -INFINITY;
+    for (int b = 0; b < NB; ++b) {
+      f32x4_t sv = s[b][0];
+      if (PAR == 2) sv += s[b][PAR - 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * b + 4 * g + i;
+        const bool ok = kval[key] != 0;
+        sc[4 * b + i] = ksc[key];
+        z[4 * b + i] = ok ? sv[i] * sc[4 * b + i] * a.sm_scale_log2 : -INFINITY;
+        mx = fmaxf(mx, z[4 * b + i]);
+      }
     }
-    float mx = z[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     const float m_new = fmaxf(m_run, mx);
@@ -193,30 +249,50 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const float alpha = exp2f(m_run - m_use);
     // Probabilities enter PV as bf16 hi + lo parts: one bf16 would round each weight
     // by up to 2^-9 relative, the whole error budget of the output.
-    float psum = 0.f, pv[8];
+    float psum = 0.f;
+    bf16x8_t pb_hi[KB], pb_lo[KB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = exp2f(z[j] - m_use);
-      psum += p;
-      pv[j] = p * sc[j];
+    for (int c = 0; c < KB; ++c) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int zi = 8 * c + j;   // blocks 2c (j < 4) and 2c+1 (j >= 4)
+        const float p = exp2f(z[zi] - m_use);
+        psum += p;
+        pv[j] = p * sc[zi];
+      }
+      split_bf16x8(pv, pb_hi[c], pb_lo[c]);
     }
-    bf16x8_t pb_hi, pb_lo;
-    split_bf16x8(pv, pb_hi, pb_lo);
     l_run = l_run * alpha + psum;
-    m_run = m_new;
+    // Rescale the accumulators only when a head's running maximum moved.
+    if (__ballot(m_new != m_run && m_run != -INFINITY)) {
 #pragma unroll
-    for (int t = 0; t < 32; ++t) o[t] *= alpha;
-
-    // O^T[dim][head] += V^T[dim][key] P^T[key][head]; the K order matches pb's keys.
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const uint16_t* vr = Vt + (16 * t + ln) * VTS;
-      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + 4 * g);
-      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16 + 4 * g);
-      const bf16x8_t av = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-      o[t] = mfma16x16x32(av, pb_hi, o[t]);
-      o[t] = mfma16x16x32(av, pb_lo, o[t]);
+      for (int t = 0; t < 32; ++t) o[t] *= alpha;
     }
+    m_run = m_new;
+
+    // O^T[dim][head] += V^T[dim][key] P^T[key][head]: per 32-key group c the lane's
+    // eight K elements are keys 32c + 4g + {0..3} and 32c + 16 + 4g + {0..3}, the order
+    // of pb.  Four d-tiles at a time: their hi-part MFMAs, then their lo-part MFMAs.
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+#pragma unroll
+      for (int t0 = 0; t0 < 32; t0 += 4) {
+        bf16x8_t av[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint16_t* vr = Vt + (16 * (t0 + u) + ln) * VTS + 32 * c;
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + 4 * g);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16 + 4 * g);
+          av[u] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[t0 + u] = mfma16x16x32(av[u], pb_hi[c], o[t0 + u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[t0 + u] = mfma16x16x32(av[u], pb_lo[c], o[t0 + u]);
+      }
+    }
+    __syncthreads();   // LDS reads of this tile are done before the next tile's writes
   }
 
   float l_tot = l_run + shfl_xor_f(l_run, 16);
@@ -230,10 +306,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if (g == 0)
       a.lse[(int64_t)r * CSA2_HEADS + h] = (m_run == -INFINITY) ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
   } else {
+    // Partials keep the accumulator fragment layout, [split][wave][t][lane][4], so every
+    // store instruction writes 1 KB of contiguous memory.
     const int64_t ps = (int64_t)r * a.splits + split;
-    float* op = a.opart + (ps * CSA2_HEADS + h) * CSA2_D + 4 * g;
+    float* op = a.opart + ((ps * 4 + wave) * 32) * 256 + 4 * lane;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) *reinterpret_cast<f32x4_t*>(op + 16 * t) = o[t];
+    for (int t = 0; t < 32; ++t) *reinterpret_cast<f32x4_t*>(op + 256 * t) = o[t];
     if (g == 0) {
       a.mpart[ps * CSA2_HEADS + h] = m_run;
       a.lpart[ps * CSA2_HEADS + h] = l_tot;
@@ -241,83 +319,84 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
 }
 
-// One workgroup per (head, row): 128 threads x 4 dims.  The per-split statistics are
-// loaded in parallel into LDS; the partial outputs are then summed with independent
-// loads in flight.
-constexpr int kMaxSplits = (CSA2_K_MAX + CSA2_SWA_MAX + TK - 1) / TK;
-
-__global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
-  __shared__ float wsh[kMaxSplits];
-  __shared__ float msh[kMaxSplits];
-  __shared__ float red[2];
-  const int h = blockIdx.x, r = blockIdx.y;
+// Merge of the split partials by log-sum-exp.  Workgroup (w, tg) of a row takes heads
+// 16w .. 16w+15 and d-tiles 4tg .. 4tg+3; thread (tt, lane) owns the fragment slot
+// (t = 4tg + tt, lane) of every split, so the partial loads are contiguous 1 KB per
+// wave and each thread derives its head's max and sum from the per-split statistics.
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int r = blockIdx.y, w = blockIdx.x >> 3, tg = blockIdx.x & 7;
   const RowKeys rk = row_keys(a, r);
   const int n_keys = rk.n_main + rk.n_swa;
   if (n_keys == 0) return;
-  const int per = a.tiles_per_split * TK;
+  const int per = a.tiles_per_split * a.tile_keys;
   const int ns = (n_keys + per - 1) / per;
+  const int tid = threadIdx.x, lane = tid & 63, tt = tid >> 6, ln = lane & 15, g = lane >> 4;
+  const int h = 16 * w + ln, t = 4 * tg + tt;
   const int64_t base = (int64_t)r * a.splits;
-  const int tid = threadIdx.x;
-  for (int s = tid; s < ns; s += 128) {
-    msh[s] = a.mpart[(base + s) * CSA2_HEADS + h];
-    wsh[s] = a.lpart[(base + s) * CSA2_HEADS + h];
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float M = -INFINITY;
-    for (int s = tid; s < ns; s += 64) M = fmaxf(M, msh[s]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    float L = 0.f;
-    if (M != -INFINITY)
-      for (int s = tid; s < ns; s += 64) L += wsh[s] * exp2f(msh[s] - M);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-    if (tid == 0) {
-      red[0] = M;
-      red[1] = L;
-    }
-  }
-  __syncthreads();
-  const float M = red[0], L = red[1];
-  const int d = 4 * tid;
-  float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + d;
-  if (M == -INFINITY || !(L > 0.f)) {
+  const float* mp = a.mpart + base * CSA2_HEADS + h;
+  const float* lp = a.lpart + base * CSA2_HEADS + h;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, mp[(int64_t)s * CSA2_HEADS]);
+  float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 16 * t + 4 * g;
+  const bool lse_writer = tg == 0 && tt == 0 && g == 0;
+  if (M == -INFINITY) {
     *reinterpret_cast<f32x4_t*>(op) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (tid == 0) a.lse[(int64_t)r * CSA2_HEADS + h] = -INFINITY;
+    if (lse_writer) a.lse[(int64_t)r * CSA2_HEADS + h] = -INFINITY;
     return;
   }
-  const float* src = a.opart + (base * CSA2_HEADS + h) * CSA2_D + d;
-  const int64_t stride = (int64_t)CSA2_HEADS * CSA2_D;
+  const float* src = a.opart + ((base * 4 + w) * 32 + t) * 256 + 4 * lane;
+  constexpr int64_t kStride = 4 * 32 * 256;   // floats per split
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
   int s = 0;
   for (; s + 4 <= ns; s += 4) {
     f32x4_t v[4];
+    float e[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(src + (s + u) * stride);
+    for (int u = 0; u < 4; ++u) {
+      v[u] = *reinterpret_cast<const f32x4_t*>(src + (s + u) * kStride);
+      e[u] = exp2f(mp[(int64_t)(s + u) * CSA2_HEADS] - M);
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += exp2f(msh[s + u] - M) * v[u];
+    for (int u = 0; u < 4; ++u) {
+      acc += e[u] * v[u];
+      L += e[u] * lp[(int64_t)(s + u) * CSA2_HEADS];
+    }
   }
-  for (; s < ns; ++s) acc += exp2f(msh[s] - M) * *reinterpret_cast<const f32x4_t*>(src + s * stride);
-  *reinterpret_cast<f32x4_t*>(op) = acc * (1.f / L);
-  if (tid == 0) a.lse[(int64_t)r * CSA2_HEADS + h] = (M + log2f(L)) * kLn2;
+  for (; s < ns; ++s) {
+    const float e = exp2f(mp[(int64_t)s * CSA2_HEADS] - M);
+    acc += e * *reinterpret_cast<const f32x4_t*>(src + s * kStride);
+    L += e * lp[(int64_t)s * CSA2_HEADS];
+  }
+  *reinterpret_cast<f32x4_t*>(op) = L > 0.f ? acc * (1.f / L) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (lse_writer) a.lse[(int64_t)r * CSA2_HEADS + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
-void attn_plan(int64_t R, int32_t sel_ld, int32_t& tiles_per_split, int32_t& splits) {
+#ifndef CSA2_ATTN_TILE
+#define CSA2_ATTN_TILE 0
+#endif
+
+// Tile size and splits per row.  Enough workgroups to cover the GPU, but with few rows
+// the 64-key tile halves the splits (and the 128 KB partial per split that the merge
+// reads back); a split takes its tiles one after another.
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& tiles_per_split, int32_t& splits) {
   const int max_keys = sel_ld + CSA2_SWA_MAX;
-  const int tiles = (max_keys + TK - 1) / TK;
+  int tk = CSA2_ATTN_TILE;
+  if (tk != 32 && tk != 64) tk = 64;
+  const int tiles = (max_keys + tk - 1) / tk;
   int64_t want = R > 0 ? (512 + R - 1) / R : 1;
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
+  tile_keys = tk;
   tiles_per_split = (int32_t)((tiles + want - 1) / want);
   splits = (tiles + tiles_per_split - 1) / tiles_per_split;
 }
 
 size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
-  int32_t tps, splits;
-  attn_plan(R, sel_ld, tps, splits);
+  int32_t tk, tps, splits;
+  attn_plan(R, sel_ld, tk, tps, splits);
   if (splits <= 1) return 0;
   const size_t parts = (size_t)R * splits * CSA2_HEADS;
   return parts * CSA2_D * sizeof(float) + 2 * parts * sizeof(float) + 3 * 256;
@@ -325,13 +404,16 @@ size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
 
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  k_attn<<<dim3(a.splits, a.g.R), dim3(256), 0, st>>>(a);
+  if (a.tile_keys == 64)
+    k_attn<2><<<dim3(a.splits, a.g.R), dim3(256), 0, st>>>(a);
+  else
+    k_attn<1><<<dim3(a.splits, a.g.R), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0 || a.splits == 1) return hipSuccess;
-  k_attn_merge<<<dim3(CSA2_HEADS, a.g.R), dim3(128), 0, st>>>(a);
+  k_attn_merge<<<dim3(32, a.g.R), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 

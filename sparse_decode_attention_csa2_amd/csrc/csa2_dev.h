@@ -89,6 +89,10 @@ __device__ __forceinline__ u32x4_t load16_a4(const uint8_t* p) {
   return *reinterpret_cast<const u32x4a4_t*>(p);
 }
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void store16_a4(float* p, f32x4_t v) {
+  typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+  *reinterpret_cast<f32x4a4_t*>(p) = v;
+}
 
 // ---------------------------------------------------------------------------------
 // MFMA: D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.

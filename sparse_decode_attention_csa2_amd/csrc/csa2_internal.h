@@ -67,6 +67,7 @@ struct ScanArgs {
   float* blk_scores;      // [R][blk_ld] (block part)
   int64_t blk_ld;
   int32_t entry_tiles;    // workgroups of the entry part (grid.x after the block part)
+  int32_t iters;          // 64-entry chunks per wave in the entry part
   int32_t block_tiles;    // workgroups of the block part (first in grid.x)
   const int32_t* kept;    // candidate-only scan: [R][kept_ld]
   const int32_t* n_kept;
@@ -107,18 +108,17 @@ struct AttnArgs {
   const uint8_t* swa;
   const float* swa_scale;
   float sm_scale_log2;       // sm_scale * log2(e)
+  int32_t tile_keys;         // 32 or 64
   int32_t tiles_per_split;
   int32_t splits;
-  float* opart;              // [R][splits][64][512]
+  float* opart;              // [R][splits][4 waves][32 d-tiles][64 lanes][4]
   float* mpart;              // [R][splits][64]
   float* lpart;              // [R][splits][64]
   float* out;                // [R][64][512]
   float* lse;                // [R][64]
 };
 
-constexpr int kAttnTile = 32;  // keys per tile
-
-void attn_plan(int64_t R, int32_t sel_ld, int32_t& tiles_per_split, int32_t& splits);
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& tiles_per_split, int32_t& splits);
 size_t attn_workspace_bytes(int64_t R, int32_t sel_ld);
 hipError_t launch_attn(AttnArgs a, hipStream_t st);
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st);

@@ -20,6 +20,16 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kGroups = 4;                          // 16-entry groups per wave per tile
 constexpr int kTile = kWaves * kGroups * 16;        // 256 entries (or blocks) per WG
+constexpr int kRsrcWord3 = 0x00020000;             // raw buffer descriptor, gfx9 family
+
+#ifndef CSA2_SCAN_DEPTH
+#define CSA2_SCAN_DEPTH 3
+#endif
+constexpr int kMaxIters = 8;                        // chunks per wave, at most
+constexpr int kWgRows = 4;                          // rows staged per workgroup
+#ifndef CSA2_SCAN_WAVES_PER_EU
+#define CSA2_SCAN_WAVES_PER_EU 4
+#endif
 
 template <int MAXPAIRS>
 __device__ __forceinline__ void load_query(const ScanArgs& a, int r0, int r1, bf16x8_t (&qa)[MAXPAIRS][4],
@@ -41,12 +51,14 @@ __device__ __forceinline__ void load_query(const ScanArgs& a, int r0, int r1, bf
   }
 }
 
-// Weighted ReLU over the lane's 4 heads, then the partner half (lane ^ 16).
+// Weighted ReLU over the lane's 4 heads, then the partner half (lane ^ 16).  The ReLU
+// is an integer max on the fp32 bits (negative floats are negative integers), and the
+// exchange is a swizzle (xor 16 within each 32-lane half).
 __device__ __forceinline__ float head_sum(const f32x4_t& acc, const float (&wv)[4]) {
   float part = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part = fmaf(wv[i], fmaxf(acc[i], 0.f), part);
-  return part + shfl_xor_f(part, 16);
+  for (int i = 0; i < 4; ++i) part = fmaf(wv[i], __int_as_float(max(__float_as_int(acc[i]), 0)), part);
+  return part + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(part), 0x401F));
 }
 
 template <int MAXPAIRS>
@@ -67,10 +79,57 @@ __device__ __forceinline__ void score_group(const bf16x8_t (&kb)[4], const bf16x
   }
 }
 
+// Entry path: the group's scores go to the wave's LDS staging rows (row t of the
+// request's rows, 64 entries of the chunk) and leave with one wide store per row.
+template <int MAXPAIRS>
+__device__ __forceinline__ void score_group_lds(const bf16x8_t (&kb)[4], const bf16x8_t (&qa)[MAXPAIRS][4],
+                                                const float (&wv)[MAXPAIRS][4], int npairs, int gi,
+                                                float (*sb)[64]) {
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int p = 0; p < MAXPAIRS; ++p) {
+    if (p < npairs) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma16x16x32(qa[p][c], kb[c], acc);
+      const float s = head_sum(acc, wv[p]);
+      if ((g & 1) == 0) sb[2 * p + (g >> 1)][16 * gi + m] = s;
+    }
+  }
+}
+
+// Stores the staged scores of a 64-entry chunk starting at pos0: lane (t, j) writes
+// entries 4j .. 4j+3 of row r0 + t, so a row leaves as 256 contiguous bytes.
+template <int MAXPAIRS>
+__device__ __forceinline__ void flush_chunk(float (*sb)[64], int nrows, int r0, int64_t pos0, int64_t n, float* out,
+                                            int64_t ld) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int lane = threadIdx.x & 63, j = lane & 15;
+#pragma unroll
+  for (int t0 = 0; t0 < 2 * MAXPAIRS; t0 += 4) {
+    const int t = t0 + (lane >> 4);
+    if (t < nrows) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&sb[t][4 * j]);
+      const int64_t pos = pos0 + 4 * j;
+      float* o = out + (int64_t)(r0 + t) * ld + pos;
+      if (pos + 4 <= n) {
+        store16_a4(o, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (pos + i < n) o[i] = v[i];
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // PARTS: 1 = entries only, 2 = block summaries only, 3 = both in one launch (distinct
 // instantiations keep the variants apart in kernel traces).
 template <int MAXPAIRS, int PARTS>
-__global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS == 1 ? CSA2_SCAN_WAVES_PER_EU : (MAXPAIRS == 8 ? 1 : 2)))) void k_scan(ScanArgs a) {
   const int b = blockIdx.y;
   int64_t e0, n;
   req_entries(a.g, b, e0, n);
@@ -78,34 +137,116 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
   req_rows(a.g, b, 2 * MAXPAIRS, r0, r1);
   if (r1 <= r0) return;
   const int npairs = (r1 - r0 + 1) >> 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
 
   // Block-summary tiles come first in the grid so that they start early and do not
   // trail the (many more) entry tiles.
   if ((int)blockIdx.x >= a.block_tiles) {
-    const int64_t base = (int64_t)(blockIdx.x - a.block_tiles) * kTile + wave * (kGroups * 16);
-    if (base >= n) return;
-    // Issue every load of the wave's tile before any conversion.
-    u32x4_t kc[kGroups];
-    uint32_t ks[kGroups];
+    // A workgroup takes iters x 4 consecutive 64-entry chunks; on step c wave w scores
+    // chunk 4c + w, so the four waves of a step read 17 KB of contiguous keys.  Each
+    // wave keeps kDepth chunks of loads in flight (a ring in registers): a chunk's slot
+    // is refilled with the loads of the chunk kDepth steps ahead as soon as it has been
+    // converted.  Keys are read through a buffer descriptor over the workgroup's
+    // entries: a lane's offset is fixed, the chunk offset is scalar and the group offset
+    // immediate, and reads past the request's end return zeros (never stored).
+    // Chunks of loads in flight per wave (fewer with more query rows held in registers).
+    constexpr int kDepth = MAXPAIRS <= 2 ? CSA2_SCAN_DEPTH : (MAXPAIRS == 4 ? 2 : 1);
+    const int iters = a.iters;
+    const int64_t wg_base = (int64_t)(blockIdx.x - a.block_tiles) * (kWaves * 64) * iters;
+    if (wg_base >= n) return;   // uniform over the workgroup
+    const int wg_n = (int)min<int64_t>(n - wg_base, (int64_t)kWaves * 64 * iters);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.idx_k + (e0 + wg_base) * CSA2_IDX_BYTES), (short)0, wg_n * CSA2_IDX_BYTES, kRsrcWord3);
+    const int voff_c = m * CSA2_IDX_BYTES + 16 * g, voff_s = m * CSA2_IDX_BYTES + 64 + g;
+    struct Chunk {
+      u32x4_t kc[kGroups];
+      uint32_t ks[kGroups];
+    };
+    auto issue = [&](Chunk& ck, int lb) {
+      const int so = lb * CSA2_IDX_BYTES;
 #pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-      int64_t e = base + gi * 16 + m;
-      e = e < n ? e : n - 1;
-      const uint8_t* rec = a.idx_k + (e0 + e) * CSA2_IDX_BYTES;
-      kc[gi] = load16_a4(rec + 16 * g);
-      ks[gi] = rec[64 + g];
-    }
+      for (int gi = 0; gi < kGroups; ++gi) {
+        ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_c + gi * 16 * CSA2_IDX_BYTES, so, 0);
+        ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff_s + gi * 16 * CSA2_IDX_BYTES, so, 0);
+      }
+    };
     bf16x8_t qa[MAXPAIRS][4];
     float wv[MAXPAIRS][4];
-    load_query<MAXPAIRS>(a, r0, r1, qa, wv);
+    const int nrows = r1 - r0;
+    // Scores are staged in LDS: with at most kWgRows rows the whole workgroup's scores
+    // stay until the end and leave as contiguous row segments (one write burst per
+    // workgroup); with more rows each wave flushes every chunk.
+    constexpr bool kWgStage = 2 * MAXPAIRS <= kWgRows;
+    constexpr int kStageRows = kWgStage ? 2 * MAXPAIRS : 1;
+    constexpr int kStageLen = kWgStage ? kWaves * 64 * kMaxIters : 1;
+    __shared__ __align__(16) float wstage[kStageRows][kStageLen];
+    __shared__ __align__(16) float sbuf[kWgStage ? 1 : kWaves][2 * MAXPAIRS][64];
+    float (*sb)[64] = sbuf[kWgStage ? 0 : wave];
+    auto consume = [&](const Chunk& ck, int lb) {
 #pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-      const float sc = e8m0_operand(ks[gi]);
-      bf16x8_t kb[4];
+      for (int gi = 0; gi < kGroups; ++gi) {
+        const float sc = e8m0_operand(ck.ks[gi]);
+        bf16x8_t kb[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kb[c] = fp4x8_to_bf16(kc[gi][c], sc);
-      score_group<MAXPAIRS>(kb, qa, wv, npairs, r0, r1, base + gi * 16 + m, n, a.scores, a.ld);
+        for (int c = 0; c < 4; ++c) kb[c] = fp4x8_to_bf16(ck.kc[gi][c], sc);
+#pragma unroll
+        for (int p = 0; p < MAXPAIRS; ++p) {
+          if (p < npairs) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc = mfma16x16x32(qa[p][c], kb[c], acc);
+            const float sv = head_sum(acc, wv[p]);
+            if ((g & 1) == 0) {
+              if constexpr (kWgStage)
+                wstage[2 * p + (g >> 1)][lb + 16 * gi + m] = sv;
+              else
+                sb[2 * p + (g >> 1)][16 * gi + m] = sv;
+            }
+          }
+        }
+      }
+      if constexpr (!kWgStage) flush_chunk<MAXPAIRS>(sb, nrows, r0, wg_base + lb, n, a.scores, a.ld);
+    };
+    constexpr int kStep = kWaves * 64;
+    const int lb0 = wave * 64;
+    if (lb0 < wg_n) {
+      Chunk ring[kDepth];
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d)
+        if (d < iters && lb0 + d * kStep < wg_n) issue(ring[d], lb0 + d * kStep);
+      load_query<MAXPAIRS>(a, r0, r1, qa, wv);
+      for (int c0 = 0; c0 < iters; c0 += kDepth) {
+        bool done = false;
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          const int c = c0 + d, lb = lb0 + c * kStep;
+          if (!done && c < iters && lb < wg_n) {
+            consume(ring[d], lb);
+            const int ln = lb + kDepth * kStep;
+            if (c + kDepth < iters && ln < wg_n) issue(ring[d], ln);
+          } else {
+            done = true;
+          }
+        }
+        if (done) break;
+      }
+    }
+    if constexpr (kWgStage) {
+      __syncthreads();
+      for (int t = 0; t < nrows; ++t) {
+        float* orow = a.scores + (int64_t)(r0 + t) * a.ld + wg_base;
+        for (int i = 4 * (int)threadIdx.x; i < wg_n; i += 4 * kWaves * 64) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&wstage[t][i]);
+          if (i + 4 <= wg_n) {
+            store16_a4(orow + i, v);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (i + k < wg_n) orow[i + k] = v[k];
+          }
+        }
+      }
     }
   } else {
     int64_t bl0, nb;
@@ -180,9 +321,20 @@ static void launch_scan_parts(const ScanArgs& a, int max_rows_per_req, dim3 grid
     k_scan<8, PARTS><<<grid, dim3(256), 0, st>>>(a);
 }
 
+#ifndef CSA2_SCAN_TARGET_WGS
+#define CSA2_SCAN_TARGET_WGS 2048
+#endif
+
 hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool blocks, hipStream_t st) {
   const int64_t max_nb = (a.g.max_entries + CSA2_BLOCK - 1) / CSA2_BLOCK;
-  a.entry_tiles = entries ? (int32_t)((a.g.max_entries + kTile - 1) / kTile) : 0;
+  // Chunks per wave: 1 while the entry part has at most CSA2_SCAN_TARGET_WGS workgroups
+  // of 256 entries, then doubled (up to 8) so that large scans run as fewer, longer
+  // workgroups that keep loads in flight across chunks.
+  const int64_t tiles1 = (a.g.max_entries + kTile - 1) / kTile;
+  int iters = 1;
+  while (iters < kMaxIters && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
+  a.iters = iters;
+  a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;
   a.block_tiles = blocks ? (int32_t)((max_nb + kTile - 1) / kTile) : 0;
   const int gx = a.entry_tiles + a.block_tiles;
   if (gx == 0 || a.g.B == 0 || a.g.R == 0) return hipSuccess;
