@@ -103,33 +103,27 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     if (wave == 0) {
       // Lane l owns bins 2047-32l down to 2016-32l; find the bin holding the rem-th key.
       const uint32_t* hb = hist + kBins - kBins / kWave * (lane + 1);
-      uint32_t c[32], tot = 0u;
+      uint32_t tot = 0u;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hb + 4 * q);
-        c[4 * q] = v[0];
-        c[4 * q + 1] = v[1];
-        c[4 * q + 2] = v[2];
-        c[4 * q + 3] = v[3];
         tot += v[0] + v[1] + v[2] + v[3];
       }
-      uint32_t before = wave_incl_scan(tot) - tot;
-      if (before < (uint32_t)rem && before + tot >= (uint32_t)rem) {
-        int qf = 0;
-        uint32_t bf = 0u;
-        bool found = false;
-#pragma unroll
-        for (int q = 31; q >= 0; --q) {
-          if (!found && before + c[q] >= (uint32_t)rem) {
-            qf = q;
-            bf = before;
-            found = true;
-          }
-          before += c[q];
-        }
-        sh.digit = (uint32_t)(kBins - kBins / kWave * (lane + 1) + qf);
-        sh.above = bf;
-        sh.m = (int)c[qf];
+      const uint32_t before = wave_incl_scan(tot) - tot;
+      // The lane whose 32 bins hold the rem-th key; its bins are then examined by
+      // lanes 0..31 in parallel (lane x takes the x-th bin in descending order).
+      const uint64_t owner = __ballot(before < (uint32_t)rem && before + tot >= (uint32_t)rem);
+      const int tl = owner ? (int)__builtin_ctzll(owner) : kWave - 1;
+      const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
+      const int x = lane & 31;
+      const uint32_t bin = (uint32_t)(kBins - kBins / kWave * (tl + 1) + (31 - x));
+      const uint32_t cnt = lane < 32 ? hist[bin] : 0u;
+      const uint32_t incl = tb + wave_incl_scan(cnt);
+      const uint64_t hit = __ballot(lane < 32 && incl >= (uint32_t)rem);
+      if (lane == (int)__builtin_ctzll(hit)) {
+        sh.digit = bin;
+        sh.above = incl - cnt;
+        sh.m = (int)cnt;
       }
     }
     __syncthreads();
@@ -146,9 +140,8 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     }
     if (m <= kMemMax) break;
   }
-  // Collect the bin's members; one wave then finds the rem-th largest member key by
-  // descending over the bits below the bin's prefix (per bit: count the members at or
-  // above the candidate with a ballot), and counts the members above it.
+  // Collect the bin's members; one wave then finds the rem-th largest member key and
+  // counts the members above it.
 #pragma unroll 4
   for (int c = c0; c < c1; ++c) {
     const int i = c * kWave + lane;
@@ -159,31 +152,53 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     }
   }
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 0 && sh.mcnt <= kWave) {
+    // At most 64 members: lane i ranks member i against all of them (keys > and ==);
+    // the rem-th largest is held by the lane with n_greater < rem <= n_greater + n_equal.
+    const int m = __builtin_amdgcn_readfirstlane(sh.mcnt);
+    const uint32_t k = lane < m ? sh.mkey[lane] : 0u;
+    uint32_t gt = 0u, eq = 0u;
+    for (int j = 0; j < m; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)k, j);
+      gt += kj > k ? 1u : 0u;
+      eq += kj == k ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(lane < m && gt < (uint32_t)rem && (uint32_t)rem <= gt + eq);
+    const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+    if (lane == src) {
+      sh.T = k;
+      sh.n_gt = above_total + (int)gt;
+    }
+  } else if (wave == 0) {
+    // More members: descend over the bits below the bin's prefix two at a time; per
+    // step, count the members at or above each of the three candidate extensions with
+    // ballots and keep the largest extension that still has rem members at or above
+    // it.  Non-members hold 0, which no candidate (always >= 1) counts.
     const int m = sh.mcnt;
     uint32_t mk[kMemMax / kWave];
-    bool in[kMemMax / kWave];
 #pragma unroll
     for (int q = 0; q < kMemMax / kWave; ++q) {
       const int i = q * kWave + lane;
-      in[q] = i < m;
-      mk[q] = sh.mkey[in[q] ? i : 0] - lo;
+      mk[q] = i < m ? sh.mkey[i] - lo : 0u;
     }
-    uint32_t t = prefix << L;                       // candidate threshold (relative to lo)
-    for (int b = L - 1; b >= 0; --b) {
-      const uint32_t cand = t | (1u << b);
-      uint32_t cnt = 0u;
+    auto count_ge = [&](uint32_t cand) {
+      uint32_t c = 0u;
 #pragma unroll
-      for (int q = 0; q < kMemMax / kWave; ++q) {
-        cnt += __popcll(__ballot(in[q] && mk[q] >= cand));
-      }
-      if (cnt >= (uint32_t)rem) t = cand;
+      for (int q = 0; q < kMemMax / kWave; ++q) c += __popcll(__ballot(mk[q] >= cand));
+      return c;
+    };
+    uint32_t t = prefix << L;   // candidate threshold (relative to lo)
+    int b = L;
+    while (b >= 2) {
+      b -= 2;
+      const uint32_t c1 = count_ge(t | (1u << b)), c2 = count_ge(t | (2u << b)), c3 = count_ge(t | (3u << b));
+      const uint32_t d = c3 >= (uint32_t)rem ? 3u : (c2 >= (uint32_t)rem ? 2u : (c1 >= (uint32_t)rem ? 1u : 0u));
+      t |= d << b;
     }
+    if (b == 1 && count_ge(t | 1u) >= (uint32_t)rem) t |= 1u;
     uint32_t gt = 0u;
 #pragma unroll
-    for (int q = 0; q < kMemMax / kWave; ++q) {
-      gt += __popcll(__ballot(in[q] && mk[q] > t));
-    }
+    for (int q = 0; q < kMemMax / kWave; ++q) gt += __popcll(__ballot(mk[q] > t));
     if (lane == 0) {
       sh.T = t + lo;
       sh.n_gt = above_total + (int)gt;
