@@ -4,17 +4,19 @@ one MI355X.
 
 One step = one csa2_decode launch chain over one batch: indexer scan of every entry, coarse
 block filter, fine top-512, and joint-softmax attention over the selected FP4 entries
-plus the FP8 window.  The default workload is the 128K-context decode (1 request x 1
+plus the FP8 window.  The headline workload is the 128K-context decode (1 request x 1
 row, 131072 tokens pooled to 65536 entries).  Inputs are synthetic (seeded) and sit in
 HBM before timing starts; the steps rotate over enough device copies of the inputs
 that no step finds its data in the 256 MB last-level cache, so every step reads HBM.
 
 The timed steps are replays of a HIP graph that holds one captured decode step per
-input copy (the eager per-call time is reported beside it).  Per-stage kernel times
-come from HIP events that csa2_decode records between its kernels on the launch
-stream, captured into the same graph, inside the timed region.  A second timed loop runs the
-scan kernel alone on a 64 x 128K batch (285 MB of keys, larger than the cache) for the
-bandwidth-at-scale figure.  The oracle (fp64, CPU) is timed on a bounded sample.
+input copy (the eager per-call time and an eager per-stage split are reported beside
+it).  The other workloads (tiny, batched, verify, 1M-unpooled, 64 x 128K) are timed the
+same way and reported per workload.  The roofline entry is the indexer scan on the
+64 x 128K batch (285 MB of FP4 keys per launch, launched alone over two alternating
+input copies, back to back between a HIP event pair on the launch stream); its HBM traffic comes from the
+committed counter summary when that summary was taken on the current scan sources.
+The oracle (fp64, CPU) is timed on a bounded sample.
 
 Prints one JSON line.
 """
@@ -133,91 +135,98 @@ def cpu_baseline(wl, seconds: float):
                       f"over {dt:.1f}s"}
 
 
-def scan_at_scale(csa2, hip, steps: int):
-    """Scan kernel alone on 64 x 128K requests (285 MB of keys per launch)."""
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "sparse_decode_attention_csa2_amd", "csrc")
+
+
+def sources_digest(names) -> str:
+    """sha256 over the named kernel sources (ties a counter summary to the code it measured)."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+SCAN_SOURCES = ("scan.hip", "csa2_dev.h", "csa2_internal.h")
+ATTN_SOURCES = ("attn.hip", "csa2_dev.h", "csa2_internal.h")
+
+
+def read_counter_summary(name: str) -> dict:
+    """key: value lines of a committed counter summary (empty if absent)."""
+    path = os.path.join(PROFILES, name)
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            line = line.strip().lstrip("-* ").strip("`")
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip().strip("`")
+    return out
+
+
+def graph_kernel_ms(hip, fns, replays: int) -> float:
+    """Average duration of one launch chain of fns, from a HIP event pair on the launch
+    stream around n back-to-back launches.  The stream is held by a spin kernel while
+    the launches are enqueued, so the GPU runs them back to back and the events do not
+    include host submission time."""
     import torch
-    from synth import make_workload
-    from synth.device import upload
-    wl = make_workload("long_128k_x64", 1, [65536] * 64, rows_per_req=1, n_needles=16, scan_only=True)
-    dw = upload(wl)
-    scores = torch.empty((wl.num_rows, wl.max_entries), dtype=torch.float32, device="cuda")
-    idx2 = dw.idx_k.clone()          # two copies (570 MB) alternate: no launch finds its keys cached
-    fns = [lambda k=k: csa2.index_score(dw.rg, k, dw.q_idx, dw.w, scores=scores) for k in (dw.idx_k, idx2)]
-    for f in fns:
+    n = max(8, min(400, replays * len(fns)))
+    for f in fns[:4]:
         f()
-    ms = graph_time_ms(hip, fns, replays=max(5, steps // 2))
-    algo = wl.total_entries * 68 + wl.num_rows * (8 * 128 * 2 + 8 * 4)
-    gbs = algo / (ms * 1e-3) / 1e9
-    return {"workload": "64 requests x 131072 tokens (65536 entries each), scan kernel alone, graph-launched",
-            "bytes_per_launch": algo, "us_per_launch": ms * 1e3, "achieved_GBs": gbs,
-            "frac_of_peak": gbs / HBM_PEAK_GBS}
+    torch.cuda.synchronize()
+    ev = make_events(hip, 2)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda._sleep(int(2.0e9 * (n * 60e-6 + 2e-3)))
+    hip.hipEventRecord(ev[0], st)
+    for i in range(n):
+        fns[i % len(fns)]()
+    hip.hipEventRecord(ev[1], st)
+    torch.cuda.synchronize()
+    return elapsed_ms(hip, ev[0], ev[1]) / n
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1, help="workload id (default 1: 128K-context decode)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-scale", action="store_true", help="skip the 64 x 128K scan-bandwidth loop")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        return 2
-
+def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128):
+    """Graph-replayed decode steps over rotating input copies; returns timings."""
     import torch
-    import sparse_decode_attention_csa2_amd as csa2
-    from synth import make_config
     from synth.device import upload
-
-    if not os.path.exists(csa2.LIB_PATH):
-        from __graft_entry__ import build
-        build()
-    torch.cuda.set_device(0)
-    hip = _hip()
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-
-    wl = make_config(args.config)
     dw = upload(wl)
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / max(1, touched_bytes(wl))) + 1)
+    n_rep = min(max_reps, max(2, math.ceil(2 * MALL_BYTES / max(1, touched_bytes(wl))) + 1))
     reps = replicate(dw, n_rep)
     decs = [csa2.Decoder(*r.decode_inputs(), k=wl.k, n_keep=wl.n_keep, sm_scale=wl.sm_scale,
                          keep_intermediates=False) for r in reps]
     for d in decs:
         d.run()
     torch.cuda.synchronize()
-    K, W = args.steps, args.warmup
-    E = csa2.DECODE_EVENTS
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     outer = make_events(hip, 2)
-
     # Eager launches (reference): one csa2_decode call per step from Python.
-    for i in range(W):
+    for i in range(min(warmup, 4 * n_rep)):
         decs[i % n_rep].run()
     torch.cuda.synchronize()
+    n_eager = min(steps, 4 * n_rep)
     hip.hipEventRecord(outer[0], st)
-    n_eager = min(K, 4 * n_rep)
     for i in range(n_eager):
         decs[i % n_rep].run()
     hip.hipEventRecord(outer[1], st)
     torch.cuda.synchronize()
     eager_ms = elapsed_ms(hip, outer[0], outer[1]) / n_eager
-
-    # Eager per-stage breakdown (events between the kernels; includes dispatch gaps).
+    # Eager per-stage split (events between the kernels; includes dispatch gaps).
+    E = csa2.DECODE_EVENTS
     evs = [make_events(hip, E) for _ in range(n_rep)]
     for i in range(n_rep):
         decs[i].run(events=evs[i])
     torch.cuda.synchronize()
-    stage_names = ["scan", "select", "attention", "merge"]
-    stage_ms = {n: float(np.mean([elapsed_ms(hip, evs[i][j], evs[i][j + 1]) for i in range(n_rep)]))
-                for j, n in enumerate(stage_names)}
-
-    # Timed region: replays of a HIP graph holding one decode step per input replica.
+    names = ["scan", "select", "attention", "merge"]
+    stages = {n: float(np.mean([elapsed_ms(hip, evs[i][j], evs[i][j + 1]) for i in range(n_rep)])) * 1e3
+              for j, n in enumerate(names)}
+    # Timed region: replays of a graph holding one decode step per input copy.
     graph = csa2.capture_graph(decs)
-    reps_needed = max(1, math.ceil(K / n_rep))
-    for _ in range(max(1, math.ceil(W / n_rep))):
+    reps_needed = max(1, math.ceil(steps / n_rep))
+    for _ in range(max(1, math.ceil(warmup / n_rep))):
         graph.replay()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -229,42 +238,164 @@ def main() -> int:
     t_wall = time.perf_counter() - t_wall
     K = reps_needed * n_rep
     total_ms = elapsed_ms(hip, outer[0], outer[1])
-    ms_step = total_ms / K
+    return {"dw": dw, "reps": reps, "steps": K, "total_ms": total_ms, "ms_per_step": total_ms / K,
+            "rows_per_s": wl.num_rows * K / (total_ms * 1e-3), "eager_ms_per_step": eager_ms,
+            "stages_us_eager": stages, "wall_s_timed": t_wall, "input_replicas": n_rep}
 
-    # Kernel timing for the rooflines: each kernel alone, launched back to back from a
-    # graph over the same cold input copies, events on the launch stream around it.
-    scan_out = torch.empty((wl.num_rows, max(1, wl.max_entries)), dtype=torch.float32, device="cuda")
-    scan_fns = [lambda r=r: csa2.index_score(r.rg, r.idx_k, r.q_idx, r.w, scores=scan_out) for r in reps]
-    scan_ms = graph_time_ms(hip, scan_fns, replays=max(3, reps_needed))
+
+def attention_ms(csa2, hip, wl, reps, replays: int) -> float:
+    """csa2_sparse_attn (attention + merge kernels) alone over the input copies, on the
+    selection of the first copy's decode."""
+    import torch
     d0 = csa2.Decoder(*reps[0].decode_inputs(), k=wl.k, n_keep=wl.n_keep, sm_scale=wl.sm_scale)
     d0.run()
     torch.cuda.synchronize()
-    attn_out = torch.empty((wl.num_rows, 64, 512), dtype=torch.float32, device="cuda")
-    attn_lse = torch.empty((wl.num_rows, 64), dtype=torch.float32, device="cuda")
-    attn_ws = torch.empty((max(256, csa2.sparse_attn_workspace_size(reps[0].rg, wl.k)),), dtype=torch.uint8,
-                          device="cuda")
-    attn_fns = [lambda r=r: csa2.sparse_attn(r.rg, r.q, r.main_kv, d0.sel_idx, d0.n_sel, r.swa, r.swa_scale,
-                                             wl.sm_scale, out=attn_out, lse=attn_lse, ws=attn_ws) for r in reps]
-    attn_ms = graph_time_ms(hip, attn_fns, replays=max(3, reps_needed))
+    out = torch.empty((wl.num_rows, 64, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((wl.num_rows, 64), dtype=torch.float32, device="cuda")
+    ws = torch.empty((max(256, csa2.sparse_attn_workspace_size(reps[0].rg, wl.k)),), dtype=torch.uint8, device="cuda")
+    fns = [lambda r=r: csa2.sparse_attn(r.rg, r.q, r.main_kv, d0.sel_idx, d0.n_sel, r.swa, r.swa_scale,
+                                        wl.sm_scale, out=out, lse=lse, ws=ws) for r in reps]
+    return graph_kernel_ms(hip, fns, replays)
 
-    scan_b, attn_b, attn_f = algorithmic(wl)
-    scan_b_entries = wl.total_entries * 68 + wl.num_rows * (8 * 128 * 2 + 8 * 4)
-    scan_gbs = scan_b_entries / (scan_ms * 1e-3) / 1e9
-    attn_gbs = attn_b / (attn_ms * 1e-3) / 1e9
-    attn_tfs = attn_f / (attn_ms * 1e-3) / 1e12
-    rl_scan = {"kernel": "indexer scan (csa2_index_score, every entry)", "bound": "hbm", "achieved": scan_gbs,
-               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": None,
-               "bytes_per_launch": scan_b_entries, "us_per_launch": scan_ms * 1e3}
-    rl_attn = {"kernel": "sparse attention (csa2_sparse_attn: attention + merge kernels)", "bound": "hbm",
-               "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
-               "traffic": None, "bytes_per_launch": attn_b, "us_per_launch": attn_ms * 1e3,
-               "mfma_TFLOPs": attn_tfs, "mfma_frac": attn_tfs / BF16_PEAK_TFLOPS}
+
+def scan_ms(csa2, hip, wl, idx_copies, dw, replays: int) -> float:
+    import torch
+    scores = torch.empty((wl.num_rows, max(1, wl.max_entries)), dtype=torch.float32, device="cuda")
+    fns = [lambda k=k: csa2.index_score(dw.rg, k, dw.q_idx, dw.w, scores=scores) for k in idx_copies]
+    for f in fns:
+        f()
+    return graph_kernel_ms(hip, fns, replays)
+
+
+def scan_bytes(wl) -> int:
+    """Algorithmic bytes of one indexer-scan launch over every entry: 68 B per entry plus
+    each row's 8 x 128 bf16 query and 8 fp32 weights."""
+    return wl.total_entries * 68 + wl.num_rows * (8 * 128 * 2 + 8 * 4)
+
+
+def attn_flops(wl) -> int:
+    return wl.num_rows * 4 * 64 * (512 + 128) * 512
+
+
+def attn_bytes(wl) -> int:
+    return wl.num_rows * (512 * 288 + 128 * (512 + 4) + 64 * 512 * 2 + 64 * 512 * 4 + 64 * 4)
+
+
+def scale_rooflines(csa2, hip, steps: int, profile_only: bool = False):
+    """Scan and attention on the 64 x 128K decode batch (one row per request)."""
+    import torch
+    from synth import make_config
+    from synth.device import upload
+    wl = make_config(5)
+    dw = upload(wl)
+    idx2 = dw.idx_k.clone()          # two copies (570 MB) alternate: no launch finds its keys cached
+    s_ms = scan_ms(csa2, hip, wl, [dw.idx_k, idx2], dw, replays=max(5, steps // 2))
+    del idx2
+    sb = scan_bytes(wl)
+    gbs = sb / (s_ms * 1e-3) / 1e9
+    traffic, traffic_note = None, "no counter summary for the current scan sources"
+    cs = read_counter_summary("scan_64x128k_counters.md")
+    if cs.get("kernel_sources_sha256") == sources_digest(SCAN_SOURCES):
+        try:
+            traffic = int(float(cs["fetch_bytes_per_launch"]) + float(cs["write_bytes_per_launch"]))
+            traffic_note = "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain copy kernel " \
+                           "(profiles/scan_64x128k_counters.md)"
+        except (KeyError, ValueError):
+            pass
+    roof = {"kernel": "indexer scan (csa2_index_score: every entry of 64 requests x 65536 entries)",
+            "workload": "long_128k_x64: 64 requests x 131072 tokens pooled to 65536 entries, 1 row each",
+            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic, "traffic_note": traffic_note, "bytes_per_launch": sb, "us_per_launch": s_ms * 1e3}
+    # Attention on the same batch: 64 rows, selections from one decode.
+    reps = [dw]
+    a_ms = attention_ms(csa2, hip, wl, reps + replicate(dw, 2)[1:], replays=max(5, steps // 2))
+    fl = attn_flops(wl)
+    tfs = fl / (a_ms * 1e-3) / 1e12
+    ab = attn_bytes(wl)
+    util = None
+    ca = read_counter_summary("attn_64rows_counters.md")
+    if ca.get("kernel_sources_sha256") == sources_digest(ATTN_SOURCES):
+        try:
+            util = float(ca["mfma_busy_frac"])
+        except (KeyError, ValueError):
+            pass
+    aroof = {"kernel": "sparse attention (csa2_sparse_attn: attention + merge kernels), 64 rows",
+             "bound": "mfma", "achieved": tfs, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": tfs / BF16_PEAK_TFLOPS, "flops_per_launch": fl, "us_per_launch": a_ms * 1e3,
+             "hbm_GBs": ab / (a_ms * 1e-3) / 1e9, "bytes_per_launch": ab,
+             "mfma_busy_frac_counters": util}
+    return roof, aroof
+
+
+def reference_copy(hip):
+    """A plain elementwise kernel of known traffic (reads and writes 256 MiB) that the
+    memory counters are scaled by."""
+    import torch
+    src = torch.ones((64 << 20,), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=1, help="headline workload id (default 1: 128K-context decode)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scale", action="store_true", help="skip the 64 x 128K roofline loops")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
+    ap.add_argument("--profile-scale", action="store_true",
+                    help="only the 64 x 128K scan/attention loops and the reference copy (for counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import sparse_decode_attention_csa2_amd as csa2
+    from synth import make_config
+
+    if not os.path.exists(csa2.LIB_PATH):
+        from __graft_entry__ import build
+        build()
+    torch.cuda.set_device(0)
+    hip = _hip()
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    if args.profile_scale:
+        roof, aroof = scale_rooflines(csa2, hip, steps=20)
+        reference_copy(hip)
+        print(json.dumps({"roofline": roof, "attention_roofline": aroof}), flush=True)
+        return 0
+
+    K, W = args.steps, args.warmup
+    wl = make_config(args.config)
+    m = measure_decode(csa2, hip, wl, K, W)
+    reps = m["reps"]
+    # Per-kernel rooflines at the headline workload: the scan and attention alone.
+    s_ms = scan_ms(csa2, hip, wl, [r.idx_k for r in reps], reps[0], replays=max(3, K // len(reps)))
+    a_ms = attention_ms(csa2, hip, wl, reps, replays=max(3, K // len(reps)))
+    sb = scan_bytes(wl)
+    head = {
+        "scan": {"us_per_launch": s_ms * 1e3, "bytes_per_launch": sb,
+                 "achieved_GBs": sb / (s_ms * 1e-3) / 1e9, "frac_of_hbm_peak": sb / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "attention": {"us_per_launch": a_ms * 1e3, "flops_per_launch": attn_flops(wl),
+                      "achieved_TFLOPs": attn_flops(wl) / (a_ms * 1e-3) / 1e12,
+                      "frac_of_bf16_peak": attn_flops(wl) / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                      "bytes_per_launch": attn_bytes(wl)},
+    }
+    del reps, m["reps"], m["dw"]
+    torch.cuda.empty_cache()
 
     res = {
         "metric": "decode query-rows/s + indexer-scan HBM GB/s (% of peak) at 128K ctx, top-512",
-        "value": wl.num_rows * K / (total_ms * 1e-3),
+        "value": m["rows_per_s"],
         "unit": "query-rows/s",
-        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": m["steps"], "warmup": W, "ms_per_step": m["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp4/fp8 in, bf16 mfma, f32 accumulate",
         "data": "synthetic",
@@ -272,16 +403,31 @@ def main() -> int:
                                f"row(s), {wl.total_entries} entries, top-{wl.k}, keep {wl.n_keep}+newest blocks, "
                                f"128-token FP8 window",
                    "requests": wl.num_requests, "rows": wl.num_rows, "entries": wl.total_entries,
-                   "input_replicas": n_rep},
-        "roofline": rl_scan,
-        "attention_roofline": rl_attn,
+                   "input_replicas": m["input_replicas"]},
         "launch": "hip graph replay (one captured decode step per input replica)",
-        "eager_ms_per_step": eager_ms,
-        "stages_us_eager": {k: v * 1e3 for k, v in stage_ms.items()},
-        "wall_s_timed": t_wall,
+        "eager_ms_per_step": m["eager_ms_per_step"],
+        "stages_us_eager": m["stages_us_eager"],
+        "kernels_headline": head,
+        "wall_s_timed": m["wall_s_timed"],
     }
     if not args.no_scale:
-        res["scan_at_scale"] = scan_at_scale(csa2, hip, steps=max(20, min(200, K // 10)))
+        roof, aroof = scale_rooflines(csa2, hip, steps=max(20, min(200, K // 10)))
+        res["roofline"] = roof
+        res["attention_roofline"] = aroof
+        torch.cuda.empty_cache()
+    if not args.no_configs:
+        per = {}
+        for i in (0, 2, 3, 4, 5):
+            if i == args.config:
+                continue
+            w = make_config(i)
+            mi = measure_decode(csa2, hip, w, steps=max(64, min(K, 400)), warmup=8)
+            per[w.name] = {"requests": w.num_requests, "rows": w.num_rows, "entries": w.total_entries,
+                           "rows_per_s": mi["rows_per_s"], "ms_per_step": mi["ms_per_step"],
+                           "stages_us_eager": mi["stages_us_eager"], "input_replicas": mi["input_replicas"]}
+            del mi, w
+            torch.cuda.empty_cache()
+        res["per_config"] = per
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

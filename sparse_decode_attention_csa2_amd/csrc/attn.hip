@@ -322,8 +322,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 // Merge of the split partials by log-sum-exp.  Workgroup (w, tg) of a row takes heads
 // 16w .. 16w+15 and d-tiles 4tg .. 4tg+3; thread (tt, lane) owns the fragment slot
 // (t = 4tg + tt, lane) of every split, so the partial loads are contiguous 1 KB per
-// wave and each thread derives its head's max and sum from the per-split statistics.
+// wave.  The 16 heads' per-split statistics are staged in LDS first (one load per
+// thread), and the partial loads are issued before the statistics are combined.
+constexpr int kMaxSplits = (CSA2_K_MAX + CSA2_SWA_MAX + 31) / 32;
+
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  __shared__ float msh[kMaxSplits][16], lsh[kMaxSplits][16];
   const int r = blockIdx.y, w = blockIdx.x >> 3, tg = blockIdx.x & 7;
   const RowKeys rk = row_keys(a, r);
   const int n_keys = rk.n_main + rk.n_swa;
@@ -333,10 +337,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, tt = tid >> 6, ln = lane & 15, g = lane >> 4;
   const int h = 16 * w + ln, t = 4 * tg + tt;
   const int64_t base = (int64_t)r * a.splits;
-  const float* mp = a.mpart + base * CSA2_HEADS + h;
-  const float* lp = a.lpart + base * CSA2_HEADS + h;
+  for (int i = tid; i < ns * 16; i += 256) {
+    const int s = i >> 4, hh = 16 * w + (i & 15);
+    msh[s][i & 15] = a.mpart[(base + s) * CSA2_HEADS + hh];
+    lsh[s][i & 15] = a.lpart[(base + s) * CSA2_HEADS + hh];
+  }
+  const float* src = a.opart + ((base * 4 + w) * 32 + t) * 256 + 4 * lane;
+  constexpr int64_t kStride = 4 * 32 * 256;   // floats per split
+  constexpr int kBatch = 8;
+  f32x4_t v[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    v[u] = u < ns ? *reinterpret_cast<const f32x4_t*>(src + u * kStride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, mp[(int64_t)s * CSA2_HEADS]);
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, msh[s][ln]);
   float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 16 * t + 4 * g;
   const bool lse_writer = tg == 0 && tt == 0 && g == 0;
   if (M == -INFINITY) {
@@ -344,29 +359,20 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     if (lse_writer) a.lse[(int64_t)r * CSA2_HEADS + h] = -INFINITY;
     return;
   }
-  const float* src = a.opart + ((base * 4 + w) * 32 + t) * 256 + 4 * lane;
-  constexpr int64_t kStride = 4 * 32 * 256;   // floats per split
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    f32x4_t v[4];
-    float e[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v[u] = *reinterpret_cast<const f32x4_t*>(src + (s + u) * kStride);
-      e[u] = exp2f(mp[(int64_t)(s + u) * CSA2_HEADS] - M);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc += e[u] * v[u];
-      L += e[u] * lp[(int64_t)(s + u) * CSA2_HEADS];
+  for (int u = 0; u < kBatch; ++u) {
+    if (u < ns) {
+      const float e = exp2f(msh[u][ln] - M);
+      acc += e * v[u];
+      L += e * lsh[u][ln];
     }
   }
-  for (; s < ns; ++s) {
-    const float e = exp2f(mp[(int64_t)s * CSA2_HEADS] - M);
+  for (int s = kBatch; s < ns; ++s) {
+    const float e = exp2f(msh[s][ln] - M);
     acc += e * *reinterpret_cast<const f32x4_t*>(src + s * kStride);
-    L += e * lp[(int64_t)s * CSA2_HEADS];
+    L += e * lsh[s][ln];
   }
   *reinterpret_cast<f32x4_t*>(op) = L > 0.f ? acc * (1.f / L) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (lse_writer) a.lse[(int64_t)r * CSA2_HEADS + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
