@@ -25,9 +25,14 @@
 namespace csa2 {
 namespace {
 
-constexpr int KLS = 520;        // Kl row stride in bf16 (512 + 8: 16-B aligned rows, spread banks)
+constexpr int KLS = 528;        // Kl row stride in bf16 (512 + 16: rows 32 B apart modulo 256 B)
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplitKeys = CSA2_K_MAX + CSA2_SWA_MAX;   // positions of one split staged in LDS
+constexpr int kAttnTileKeys = 64;
+
+#ifndef CSA2_ATTN_TARGET_WGS
+#define CSA2_ATTN_TARGET_WGS 256
+#endif
 
 struct RowKeys {
   int64_t e0, n;     // request's first pool entry and entry count
@@ -88,14 +93,29 @@ __device__ __forceinline__ void convert_key(const KeyRegs& k, uint32_t (&w)[16])
   }
 }
 
-// KB = 32-key groups per tile (tile = 32 KB keys).
-template <int KB>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  constexpr int TK = 32 * KB;
-  constexpr int VTS = TK + 4;          // Vt row stride in bf16
-  constexpr int NB = 2 * KB;           // 16-key blocks per tile
+// 16 bf16 of the key-major tile read transposed: with lane (g, i) (i = lane % 16)
+// pointing at 4 consecutive elements, lane (g, j) receives element j % 4 of lanes
+// (g, 4k + j / 4), k = 0..3 (ds_read_b64_tr_b16).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(__attribute__((address_space(3))) uint16_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// One workgroup of 8 waves per split: wave (hg, dh) = (wave % 4, wave / 4) owns heads
+// 16hg .. 16hg+15 and latent dims 256dh .. 256dh+255 of the output.  Per 64-key tile:
+// the 512 threads dequantise the tile into the key-major LDS copy (each thread 2 keys x
+// 32 dims; the records of the next tile are loaded before the current tile computes);
+// each wave contracts its half of the dims for S^T = K Q^T and the two halves meet
+// through LDS; the online softmax runs identically in both waves of a head group; PV
+// reads its A operand (V^T) from the same key-major copy with transposing LDS loads.
+__global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
+  constexpr int TK = kAttnTileKeys;   // 64
+  constexpr int KB = TK / 32;         // 32-key groups
+  constexpr int NB = TK / 16;         // 16-key blocks
   __shared__ __align__(16) uint16_t Kl[TK * KLS];
-  __shared__ __align__(16) uint16_t Vt[CSA2_D * VTS];
+  __shared__ __align__(16) float Sx[8][4 * NB][64];
   __shared__ float ksc[TK];
   __shared__ int kval[TK];
   __shared__ int32_t spos[kMaxSplitKeys];
@@ -103,12 +123,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int r = blockIdx.y, split = blockIdx.x;
   const RowKeys rk = row_keys(a, r);
   const int n_keys = rk.n_main + rk.n_swa;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
-  const int h = wave * 16 + ln;
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), hg = wave & 3, dh = wave >> 2;
+  const int h = hg * 16 + ln;
 
   if (n_keys == 0) {
     if (split == 0) {
-      for (int i = tid; i < CSA2_HEADS * CSA2_D; i += 256) a.out[(int64_t)r * CSA2_HEADS * CSA2_D + i] = 0.f;
+      for (int i = tid; i < CSA2_HEADS * CSA2_D; i += 512) a.out[(int64_t)r * CSA2_HEADS * CSA2_D + i] = 0.f;
       if (tid < CSA2_HEADS) a.lse[(int64_t)r * CSA2_HEADS + tid] = -INFINITY;
     }
     return;
@@ -120,30 +141,31 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   // Stage the split's selected positions in LDS (one round trip for all tiles).
   {
     const int m_end = min(k_end, rk.n_main);
-    for (int i = k_begin + tid; i < m_end; i += 256) spos[i - k_begin] = a.sel[(int64_t)r * a.sel_ld + i];
+    for (int i = k_begin + tid; i < m_end; i += 512) spos[i - k_begin] = a.sel[(int64_t)r * a.sel_ld + i];
   }
-  // Query fragments (B operand of S^T = K Q^T): lane holds q[h][32*st + 8g + j].
-  bf16x8_t qb[16];
+  // Query fragments of this wave's dims (B operand of S^T = K Q^T): lane holds
+  // q[h][256dh + 32st + 8g + j].
+  bf16x8_t qb[8];
   {
-    const uint16_t* qp = a.q + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 8 * g;
+    const uint16_t* qp = a.q + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 256 * dh + 8 * g;
 #pragma unroll
-    for (int st = 0; st < 16; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
+    for (int st = 0; st < 8; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
   }
   __syncthreads();
 
-  f32x4_t o[32];
+  f32x4_t o[16];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Dequant role: keys 32u + 2kp + e (u < KB, e < 2) of a tile, dims 32ch .. 32ch+31.
-  const int kp = tid & 15, ch = tid >> 4;
+  // Dequant role: keys 32u + 2kp + e (e < 2) of a tile, dims 32ch .. 32ch+31.
+  const int kp = tid & 15, ch = (tid >> 4) & 15, u = tid >> 8;
   const int32_t* sp = spos - k_begin;   // position of key i is sp[i] (i in the split)
-  KeyRegs kr[2 * KB];
+  KeyRegs kr[2];
   auto load_keys = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < 2 * KB; ++u) {
-      const int i = kt + 32 * (u >> 1) + 2 * kp + (u & 1);
+    for (int e = 0; e < 2; ++e) {
+      const int i = kt + 32 * u + 2 * kp + e;
       KeyRegs k;
       k.kind = 0;
       k.c0 = u32x4_t{0u, 0u, 0u, 0u};
@@ -167,78 +189,70 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
           k.kind = 2;
         }
       }
-      kr[u] = k;
+      kr[e] = k;
     }
   };
   load_keys(k_begin);
 
+  // Transposed-read offsets (elements): lane (g, i = 4k + q) points at key 4g + k of a
+  // 16-key half and dims 4q .. 4q+3 of a 16-dim tile.
+  const int tr_off = (4 * g + (ln >> 2)) * KLS + 256 * dh + 4 * (ln & 3);
+
   for (int kt = k_begin; kt < k_end; kt += TK) {
-    // Convert this tile's records (already in registers) into LDS: key-major Kl and
-    // dim-major Vt (two keys packed per 32-bit word).
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      uint32_t w0[16], w1[16];
-      convert_key(kr[2 * u], w0);
-      convert_key(kr[2 * u + 1], w1);
-      const int key0 = 32 * u + 2 * kp;
-      uint16_t* k0 = Kl + key0 * KLS + 32 * ch;
+    for (int e = 0; e < 2; ++e) {
+      uint32_t w[16];
+      convert_key(kr[e], w);
+      uint16_t* k0 = Kl + (32 * u + 2 * kp + e) * KLS + 32 * ch;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<u32x4_t*>(k0 + 8 * q) = u32x4_t{w0[4 * q], w0[4 * q + 1], w0[4 * q + 2], w0[4 * q + 3]};
-        *reinterpret_cast<u32x4_t*>(k0 + KLS + 8 * q) = u32x4_t{w1[4 * q], w1[4 * q + 1], w1[4 * q + 2], w1[4 * q + 3]};
-      }
-      uint32_t* vt = reinterpret_cast<uint32_t*>(Vt + (32 * ch) * VTS + key0);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        vt[(2 * q) * (VTS / 2)] = (w0[q] & 0xFFFFu) | (w1[q] << 16);
-        vt[(2 * q + 1) * (VTS / 2)] = (w0[q] >> 16) | (w1[q] & 0xFFFF0000u);
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x4_t*>(k0 + 8 * q) = u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
       if (ch == 0) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const KeyRegs& k = kr[2 * u + e];
-          ksc[key0 + e] = k.kind == 2 ? __uint_as_float(k.sc) : (k.kind == 1 ? 1.f : 0.f);
-          kval[key0 + e] = k.kind != 0;
-        }
+        const int key = 32 * u + 2 * kp + e;
+        ksc[key] = kr[e].kind == 2 ? __uint_as_float(kr[e].sc) : (kr[e].kind == 1 ? 1.f : 0.f);
+        kval[key] = kr[e].kind != 0;
       }
     }
     __syncthreads();
     // Prefetch the next tile's records while this one computes.
     if (kt + TK < k_end) load_keys(kt + TK);
 
-    // S^T[key][head] for the tile's keys (16-key blocks b) and this wave's 16 heads.
-    // With one 32-key group the even and odd K steps use separate accumulators so that
-    // four MFMA chains are in flight.
-    constexpr int PAR = KB == 1 ? 2 : 1;
-    f32x4_t s[NB][PAR];
+    // Partial S^T over this wave's 256 dims: 16-key blocks b, 8 K steps of 32 dims.
+    f32x4_t s[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bf16x8_t ak =
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+        s[b] = mfma16x16x32(ak, qb[st], s[b]);
+      }
+    }
+    // The two dim halves of a head group meet in LDS.
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int p = 0; p < PAR; ++p) s[b][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) Sx[wave][4 * b + i][lane] = s[b][i];
+    __syncthreads();
 #pragma unroll
-    for (int st = 0; st < 16; st += PAR) {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int p = 0; p < PAR; ++p) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const bf16x8_t ak = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 32 * (st + p) + 8 * g));
-          s[b][p] = mfma16x16x32(ak, qb[st + p], s[b][p]);
-        }
-      }
-    }
-    // Lane holds keys 16b + 4g + i for head h.
+      for (int i = 0; i < 4; ++i) s[b][i] += Sx[wave ^ 4][4 * b + i][lane];
+
+    // Lane holds keys 16b + 4g + i for head h (the same values in both waves of the
+    // head group: a + b == b + a).
     float z[4 * NB], sc[4 * NB];
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      f32x4_t sv = s[b][0];
-      if (PAR == 2) sv += s[b][PAR - 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 16 * b + 4 * g + i;
         const bool ok = kval[key] != 0;
         sc[4 * b + i] = ksc[key];
-        z[4 * b + i] = ok ? sv[i] * sc[4 * b + i] * a.sm_scale_log2 : -INFINITY;
+        z[4 * b + i] = ok ? s[b][i] * sc[4 * b + i] * a.sm_scale_log2 : -INFINITY;
         mx = fmaxf(mx, z[4 * b + i]);
       }
     }
@@ -267,29 +281,29 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     // Rescale the accumulators only when a head's running maximum moved.
     if (__ballot(m_new != m_run && m_run != -INFINITY)) {
 #pragma unroll
-      for (int t = 0; t < 32; ++t) o[t] *= alpha;
+      for (int t = 0; t < 16; ++t) o[t] *= alpha;
     }
     m_run = m_new;
 
-    // O^T[dim][head] += V^T[dim][key] P^T[key][head]: per 32-key group c the lane's
-    // eight K elements are keys 32c + 4g + {0..3} and 32c + 16 + 4g + {0..3}, the order
-    // of pb.  Four d-tiles at a time: their hi-part MFMAs, then their lo-part MFMAs.
+    // O^T[dim][head] += V^T[dim][key] P^T[key][head] over this wave's 16 d-tiles: per
+    // 32-key group c the lane's eight K elements are keys 32c + 4g + {0..3} and
+    // 32c + 16 + 4g + {0..3} (the order of pb), read transposed from the key-major tile.
 #pragma unroll
     for (int c = 0; c < KB; ++c) {
 #pragma unroll
-      for (int t0 = 0; t0 < 32; t0 += 4) {
+      for (int t0 = 0; t0 < 16; t0 += 4) {
         bf16x8_t av[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint16_t* vr = Vt + (16 * (t0 + u) + ln) * VTS + 32 * c;
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + 4 * g);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16 + 4 * g);
-          av[u] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+        for (int v = 0; v < 4; ++v) {
+          const uint16_t* p = Kl + tr_off + 32 * c * KLS + 16 * (t0 + v);
+          const u32x2_t lo = lds_read_tr16(p);
+          const u32x2_t hi = lds_read_tr16(p + 16 * KLS);
+          av[v] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[t0 + u] = mfma16x16x32(av[u], pb_hi[c], o[t0 + u]);
+        for (int v = 0; v < 4; ++v) o[t0 + v] = mfma16x16x32(av[v], pb_hi[c], o[t0 + v]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[t0 + u] = mfma16x16x32(av[u], pb_lo[c], o[t0 + u]);
+        for (int v = 0; v < 4; ++v) o[t0 + v] = mfma16x16x32(av[v], pb_lo[c], o[t0 + v]);
       }
     }
     __syncthreads();   // LDS reads of this tile are done before the next tile's writes
@@ -297,22 +311,22 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
   float l_tot = l_run + shfl_xor_f(l_run, 16);
   l_tot += shfl_xor_f(l_tot, 32);
-  // Lane holds O^T[16t + 4g + i][h].
+  // Lane holds O^T[256dh + 16t + 4g + i][h].
   if (a.splits == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 4 * g;
+    float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 256 * dh + 4 * g;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) *reinterpret_cast<f32x4_t*>(op + 16 * t) = o[t] * inv;
-    if (g == 0)
+    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4_t*>(op + 16 * t) = o[t] * inv;
+    if (g == 0 && dh == 0)
       a.lse[(int64_t)r * CSA2_HEADS + h] = (m_run == -INFINITY) ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
   } else {
     // Partials keep the accumulator fragment layout, [split][wave][t][lane][4], so every
     // store instruction writes 1 KB of contiguous memory.
     const int64_t ps = (int64_t)r * a.splits + split;
-    float* op = a.opart + ((ps * 4 + wave) * 32) * 256 + 4 * lane;
+    float* op = a.opart + ((ps * 8 + wave) * 16) * 256 + 4 * lane;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) *reinterpret_cast<f32x4_t*>(op + 256 * t) = o[t];
-    if (g == 0) {
+    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4_t*>(op + 256 * t) = o[t];
+    if (g == 0 && dh == 0) {
       a.mpart[ps * CSA2_HEADS + h] = m_run;
       a.lpart[ps * CSA2_HEADS + h] = l_tot;
     }
@@ -342,8 +356,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     msh[s][i & 15] = a.mpart[(base + s) * CSA2_HEADS + hh];
     lsh[s][i & 15] = a.lpart[(base + s) * CSA2_HEADS + hh];
   }
-  const float* src = a.opart + ((base * 4 + w) * 32 + t) * 256 + 4 * lane;
-  constexpr int64_t kStride = 4 * 32 * 256;   // floats per split
+  // Split partial layout [split][wave = hg + 4 dh][16 d-tiles][lane][4].
+  const float* src = a.opart + ((base * 8 + w + 4 * (t >> 4)) * 16 + (t & 15)) * 256 + 4 * lane;
+  constexpr int64_t kStride = 8 * 16 * 256;   // floats per split
   constexpr int kBatch = 8;
   f32x4_t v[kBatch];
 #pragma unroll
@@ -380,19 +395,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 }  // namespace
 
-#ifndef CSA2_ATTN_TILE
-#define CSA2_ATTN_TILE 0
-#endif
-
-// Tile size and splits per row.  Enough workgroups to cover the GPU, but with few rows
-// the 64-key tile halves the splits (and the 128 KB partial per split that the merge
-// reads back); a split takes its tiles one after another.
+// Splits per row: enough workgroups to cover the GPU; a split takes its 64-key tiles
+// one after another.
 void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& tiles_per_split, int32_t& splits) {
   const int max_keys = sel_ld + CSA2_SWA_MAX;
-  int tk = CSA2_ATTN_TILE;
-  if (tk != 32 && tk != 64) tk = 64;
+  const int tk = kAttnTileKeys;
   const int tiles = (max_keys + tk - 1) / tk;
-  int64_t want = R > 0 ? (512 + R - 1) / R : 1;
+  int64_t want = R > 0 ? (CSA2_ATTN_TARGET_WGS + R - 1) / R : 1;
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
   tile_keys = tk;
@@ -410,10 +419,7 @@ size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
 
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  if (a.tile_keys == 64)
-    k_attn<2><<<dim3(a.splits, a.g.R), dim3(256), 0, st>>>(a);
-  else
-    k_attn<1><<<dim3(a.splits, a.g.R), dim3(256), 0, st>>>(a);
+  k_attn<<<dim3(a.splits, a.g.R), dim3(512), 0, st>>>(a);
   return hipGetLastError();
 }
 

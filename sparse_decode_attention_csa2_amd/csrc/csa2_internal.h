@@ -108,10 +108,10 @@ struct AttnArgs {
   const uint8_t* swa;
   const float* swa_scale;
   float sm_scale_log2;       // sm_scale * log2(e)
-  int32_t tile_keys;         // 32 or 64
+  int32_t tile_keys;         // keys per tile (64)
   int32_t tiles_per_split;
   int32_t splits;
-  float* opart;              // [R][splits][4 waves][32 d-tiles][64 lanes][4]
+  float* opart;              // [R][splits][8 waves][16 d-tiles][64 lanes][4]
   float* mpart;              // [R][splits][64]
   float* lpart;              // [R][splits][64]
   float* out;                // [R][64][512]
