@@ -118,7 +118,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   __shared__ __align__(16) float Sx[8][4 * NB][64];
   __shared__ float ksc[TK];
   __shared__ int kval[TK];
-  __shared__ int32_t spos[kMaxSplitKeys];
 
   const int r = blockIdx.y, split = blockIdx.x;
   const RowKeys rk = row_keys(a, r);
@@ -138,11 +137,51 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   if (k_begin >= n_keys) return;
   const int k_end = min(n_keys, k_begin + a.tiles_per_split * TK);
 
-  // Stage the split's selected positions in LDS (one round trip for all tiles).
-  {
-    const int m_end = min(k_end, rk.n_main);
-    for (int i = k_begin + tid; i < m_end; i += 512) spos[i - k_begin] = a.sel[(int64_t)r * a.sel_ld + i];
-  }
+  f32x4_t o[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Dequant role: keys 32u + 2kp + e (e < 2) of a tile, dims 32ch .. 32ch+31.  A tile's
+  // keys are fetched in two steps that every thread takes without branching (so no load
+  // waits on another path's registers): the selected positions (sel_pos), then the
+  // records (load_keys), each address clamped to valid memory and the key's kind
+  // deciding afterwards what the loaded bytes mean.
+  const int kp = tid & 15, ch = (tid >> 4) & 15, u = tid >> 8;
+  const int32_t* sel_row = a.sel + (int64_t)r * a.sel_ld;
+  const int last_main = rk.n_main > 0 ? rk.n_main - 1 : 0;
+  int32_t pos_raw[2];
+  auto sel_pos = [&](int kt) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) pos_raw[e] = sel_row[min(kt + 32 * u + 2 * kp + e, last_main)];
+  };
+  const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.q);   // any readable 16-B aligned bytes
+  KeyRegs kr[2];
+  auto load_keys = [&](int kt) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = kt + 32 * u + 2 * kp + e;
+      const bool live = i < k_end;
+      const int64_t pos = pos_raw[e];
+      const bool is_main = live && i < rk.n_main && pos >= 0 && pos < rk.n;
+      const bool is_win = live && i >= rk.n_main;
+      const int64_t tok = rk.s0 + (is_win ? i - rk.n_main : 0);
+      const uint8_t* mrec = a.main_kv + (rk.e0 + (is_main ? pos : 0)) * CSA2_MAIN_BYTES;
+      const uint8_t* wrec = a.swa + tok * CSA2_D + 32 * ch;
+      const uint8_t* pa = is_main ? mrec + 16 * ch : (is_win ? wrec : safe);
+      const uint8_t* pb = is_win ? wrec + 16 : pa;
+      const uint8_t* ps = is_main ? mrec + 256 + 4 * (ch >> 1)
+                                  : (is_win ? reinterpret_cast<const uint8_t*>(a.swa_scale + tok) : safe);
+      KeyRegs k;
+      k.c0 = load16(pa);
+      k.c1 = load16(pb);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(ps);
+      k.sc = is_main ? (sw >> (16 * (ch & 1))) & 0xFFFFu : sw;
+      k.kind = is_main ? 1 : (is_win ? 2 : 0);
+      kr[e] = k;
+    }
+  };
+  sel_pos(k_begin);
   // Query fragments of this wave's dims (B operand of S^T = K Q^T): lane holds
   // q[h][256dh + 32st + 8g + j].
   bf16x8_t qb[8];
@@ -151,47 +190,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
   }
-  __syncthreads();
-
-  f32x4_t o[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // Dequant role: keys 32u + 2kp + e (e < 2) of a tile, dims 32ch .. 32ch+31.
-  const int kp = tid & 15, ch = (tid >> 4) & 15, u = tid >> 8;
-  const int32_t* sp = spos - k_begin;   // position of key i is sp[i] (i in the split)
-  KeyRegs kr[2];
-  auto load_keys = [&](int kt) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int i = kt + 32 * u + 2 * kp + e;
-      KeyRegs k;
-      k.kind = 0;
-      k.c0 = u32x4_t{0u, 0u, 0u, 0u};
-      k.c1 = k.c0;
-      k.sc = 0u;
-      if (i < k_end) {
-        if (i < rk.n_main) {
-          const int64_t pos = sp[i];
-          if (pos >= 0 && pos < rk.n) {
-            const uint8_t* rec = a.main_kv + (rk.e0 + pos) * CSA2_MAIN_BYTES;
-            k.c0 = load16(rec + 16 * ch);
-            k.sc = *reinterpret_cast<const uint16_t*>(rec + 256 + 2 * ch);
-            k.kind = 1;
-          }
-        } else {
-          const int64_t tok = rk.s0 + (i - rk.n_main);
-          const uint8_t* rec = a.swa + tok * CSA2_D + 32 * ch;
-          k.c0 = load16(rec);
-          k.c1 = load16(rec + 16);
-          k.sc = __float_as_uint(a.swa_scale[tok]);
-          k.kind = 2;
-        }
-      }
-      kr[e] = k;
-    }
-  };
   load_keys(k_begin);
 
   // Transposed-read offsets (elements): lane (g, i = 4k + q) points at key 4g + k of a
@@ -214,8 +212,9 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
       }
     }
     __syncthreads();
-    // Prefetch the next tile's records while this one computes.
-    if (kt + TK < k_end) load_keys(kt + TK);
+    // The next tile's positions now, its records after the softmax.
+    const bool more = kt + TK < k_end;
+    if (more) sel_pos(kt + TK);
 
     // Partial S^T over this wave's 256 dims: 16-key blocks b, 8 K steps of 32 dims.
     f32x4_t s[NB];
@@ -284,6 +283,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
       for (int t = 0; t < 16; ++t) o[t] *= alpha;
     }
     m_run = m_new;
+    if (more) load_keys(kt + TK);
 
     // O^T[dim][head] += V^T[dim][key] P^T[key][head] over this wave's 16 d-tiles: per
     // 32-key group c the lane's eight K elements are keys 32c + 4g + {0..3} and
