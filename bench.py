@@ -223,6 +223,19 @@ def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128):
     names = ["scan", "select", "attention", "merge"]
     stages = {n: float(np.mean([elapsed_ms(hip, evs[i][j], evs[i][j + 1]) for i in range(n_rep)])) * 1e3
               for j, n in enumerate(names)}
+    # Per-step latency distribution: one event pair around each decode step, the steps
+    # enqueued behind a spin kernel so they run back to back.
+    n_lat = min(200, max(20, 2 * n_rep))
+    lev = make_events(hip, 2 * n_lat)
+    torch.cuda._sleep(int(2.0e9 * (n_lat * 80e-6 + 2e-3)))
+    for i in range(n_lat):
+        hip.hipEventRecord(lev[2 * i], st)
+        decs[i % n_rep].run()
+        hip.hipEventRecord(lev[2 * i + 1], st)
+    torch.cuda.synchronize()
+    lat = np.array([elapsed_ms(hip, lev[2 * i], lev[2 * i + 1]) for i in range(n_lat)]) * 1e3
+    lat_us = {"p10": float(np.percentile(lat, 10)), "p50": float(np.percentile(lat, 50)),
+              "p90": float(np.percentile(lat, 90)), "steps": n_lat}
     # Timed region: replays of a graph holding one decode step per input copy.
     graph = csa2.capture_graph(decs)
     reps_needed = max(1, math.ceil(steps / n_rep))
@@ -240,7 +253,8 @@ def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128):
     total_ms = elapsed_ms(hip, outer[0], outer[1])
     return {"dw": dw, "reps": reps, "steps": K, "total_ms": total_ms, "ms_per_step": total_ms / K,
             "rows_per_s": wl.num_rows * K / (total_ms * 1e-3), "eager_ms_per_step": eager_ms,
-            "stages_us_eager": stages, "wall_s_timed": t_wall, "input_replicas": n_rep}
+            "stages_us_eager": stages, "step_latency_us": lat_us, "wall_s_timed": t_wall,
+            "input_replicas": n_rep}
 
 
 def attention_ms(csa2, hip, wl, reps, replays: int) -> float:
@@ -302,10 +316,32 @@ def scale_rooflines(csa2, hip, steps: int, profile_only: bool = False):
                            "(profiles/scan_64x128k_counters.md)"
         except (KeyError, ValueError):
             pass
+    # Plain streaming read of the same bytes (csa2_debug_stream_read over two alternating
+    # copies of the keys): what the memory system delivers to a kernel that only reads.
+    idx3 = dw.idx_k.clone()
+    sink = torch.zeros((4,), dtype=torch.int32, device="cuda")
+    r_ms = graph_kernel_ms(hip, [lambda t=t: csa2.debug_stream_read(t, sink) for t in (dw.idx_k, idx3)],
+                           replays=max(5, steps // 2))
+    del idx3
+    read_gbs = sb / (r_ms * 1e-3) / 1e9
     roof = {"kernel": "indexer scan (csa2_index_score: every entry of 64 requests x 65536 entries)",
             "workload": "long_128k_x64: 64 requests x 131072 tokens pooled to 65536 entries, 1 row each",
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-            "traffic": traffic, "traffic_note": traffic_note, "bytes_per_launch": sb, "us_per_launch": s_ms * 1e3}
+            "traffic": traffic, "traffic_note": traffic_note, "bytes_per_launch": sb, "us_per_launch": s_ms * 1e3,
+            "plain_read_GBs": read_gbs, "frac_of_plain_read": gbs / read_gbs,
+            "plain_read_note": "csa2_debug_stream_read (16-B loads, 16 KiB per workgroup) over the same "
+                               "285 MB, two alternating copies, same timing"}
+    # The 1M-context batch (4 requests x 1,048,576 entries, 285 MB of keys).
+    w4 = make_config(4, scan_only=True)
+    if w4.num_rows:
+        d4 = upload(w4)
+        i4 = d4.idx_k.clone()
+        s4 = scan_ms(csa2, hip, w4, [d4.idx_k, i4], d4, replays=max(5, steps // 2))
+        roof["unpooled_1m_scan"] = {"us_per_launch": s4 * 1e3, "bytes_per_launch": scan_bytes(w4),
+                                    "achieved_GBs": scan_bytes(w4) / (s4 * 1e-3) / 1e9,
+                                    "frac": scan_bytes(w4) / (s4 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del d4, i4, w4
+        torch.cuda.empty_cache()
     # Attention on the same batch: 64 rows, selections from one decode.
     reps = [dw]
     a_ms = attention_ms(csa2, hip, wl, reps + replicate(dw, 2)[1:], replays=max(5, steps // 2))
@@ -407,6 +443,7 @@ def main() -> int:
         "launch": "hip graph replay (one captured decode step per input replica)",
         "eager_ms_per_step": m["eager_ms_per_step"],
         "stages_us_eager": m["stages_us_eager"],
+        "step_latency_us": m["step_latency_us"],
         "kernels_headline": head,
         "wall_s_timed": m["wall_s_timed"],
     }
@@ -424,6 +461,7 @@ def main() -> int:
             mi = measure_decode(csa2, hip, w, steps=max(64, min(K, 400)), warmup=8)
             per[w.name] = {"requests": w.num_requests, "rows": w.num_rows, "entries": w.total_entries,
                            "rows_per_s": mi["rows_per_s"], "ms_per_step": mi["ms_per_step"],
+                           "step_latency_us": mi["step_latency_us"],
                            "stages_us_eager": mi["stages_us_eager"], "input_replicas": mi["input_replicas"]}
             del mi, w
             torch.cuda.empty_cache()

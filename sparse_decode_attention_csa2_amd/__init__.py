@@ -61,7 +61,8 @@ class _DecodeArgs(ctypes.Structure):
 
 EXPORTS = ("csa2_index_score", "csa2_block_filter", "csa2_topk", "csa2_sparse_attn",
            "csa2_sparse_attn_workspace_size", "csa2_decode", "csa2_decode_workspace_size",
-           "csa2_debug_dequant", "csa2_status_string", "csa2_last_error", "csa2_version")
+           "csa2_debug_dequant", "csa2_debug_stream_read", "csa2_status_string", "csa2_last_error",
+           "csa2_version")
 
 _lib = None
 
@@ -86,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "csa2_decode": ([DA, P, SZ, P], ctypes.c_int),
         "csa2_decode_workspace_size": ([DA], SZ),
         "csa2_debug_dequant": ([I32, P, P, I64, P, P], ctypes.c_int),
+        "csa2_debug_stream_read": ([P, I64, P, P], ctypes.c_int),
         "csa2_status_string": ([I32], ctypes.c_char_p),
         "csa2_last_error": ([], ctypes.c_char_p),
         "csa2_version": ([], I32),
@@ -329,6 +331,16 @@ def decode(rg: Ragged, idx_k, main_kv, blk_sum, swa, swa_scale, q, q_idx, w_idx,
     d = Decoder(rg, idx_k, main_kv, blk_sum, swa, swa_scale, q, q_idx, w_idx, **kw)
     d.run()
     return d
+
+
+def debug_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Plain streaming read of ``src`` (a bandwidth reference; reads every byte, writes
+    nothing to ``sink`` in practice)."""
+    lib = load_library()
+    _dev(src, (), "src")
+    _dev(sink, (torch.int32,), "sink")
+    nbytes = src.numel() * src.element_size()
+    _check(lib.csa2_debug_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream()))
 
 
 def debug_dequant(kind: int, records: torch.Tensor, scales: torch.Tensor | None = None) -> torch.Tensor:

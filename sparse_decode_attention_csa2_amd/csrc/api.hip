@@ -130,6 +130,33 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int kind, const uint8_t* 
 }  // namespace
 
 namespace csa2 {
+// Plain streaming read: workgroup w reads the 16 KiB chunk w with four 16-B loads per
+// thread in flight.
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__ p, int64_t n16, uint32_t* sink) {
+  const int64_t b0 = (int64_t)blockIdx.x * 1024;
+  const int64_t e = b0 + 1024 < n16 ? b0 + 1024 : n16;
+  uint32_t acc = 0u;
+  int64_t i = b0 + threadIdx.x;
+  if (i + 768 < e) {
+    const u32x4_t x0 = p[i], x1 = p[i + 256], x2 = p[i + 512], x3 = p[i + 768];
+    const u32x4_t y = x0 ^ x1 ^ x2 ^ x3;
+    acc = y[0] ^ y[1] ^ y[2] ^ y[3];
+  } else {
+    for (; i < e; i += 256) {
+      const u32x4_t x = p[i];
+      acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  k_stream_read<<<dim3((unsigned)ceil_div(n16, 1024)), dim3(256), 0, st>>>(reinterpret_cast<const u32x4_t*>(src), n16,
+                                                                            sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
                                 hipStream_t st) {
   const int groups = (kind == CSA2_DQ_IDX) ? CSA2_IDX_D / 8 : CSA2_D / 8;
@@ -438,6 +465,16 @@ int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales
   CHECK(check_ptr(out, 4, "out"));
   if (kind == CSA2_DQ_SWA) CHECK(check_ptr(scales, 4, "scales"));
   LAUNCH(launch_debug_dequant(kind, records, scales, n, out, reinterpret_cast<hipStream_t>(stream)), "dequant");
+  return CSA2_OK;
+}
+
+int csa2_debug_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return fail(CSA2_ERR_INVALID_ARG, "bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return CSA2_OK;
+  if (bytes / 16 / 1024 >= (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_UNSUPPORTED, "too many bytes for one launch");
+  CHECK(check_ptr(src, 16, "src"));
+  CHECK(check_ptr(sink, 4, "sink"));
+  LAUNCH(launch_stream_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream)), "stream read");
   return CSA2_OK;
 }
 

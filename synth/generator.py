@@ -350,6 +350,8 @@ def config_lengths(i: int) -> tuple[list, list, int, int, int]:
     raise ValueError(f"unknown config {i}")
 
 
-def make_config(i: int, workers: int | None = None) -> Workload:
+def make_config(i: int, workers: int | None = None, scan_only: bool = False) -> Workload:
+    """Workload i; scan_only skips the attention-side pools (main KV, window)."""
     toks, ents, rows, needles, seed = config_lengths(i)
-    return make_workload(CONFIGS[i], seed, ents, rows, n_needles=needles, n_tokens=toks, workers=workers)
+    return make_workload(CONFIGS[i], seed, ents, rows, n_needles=needles, n_tokens=toks, workers=workers,
+                         scan_only=scan_only)

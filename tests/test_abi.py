@@ -125,3 +125,11 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.csa2_index_score(ctypes.byref(rg), None, None, None, None, None, 0, None, 0, None) == csa2.OK
     assert lib.csa2_debug_dequant(0, None, None, 0, None, None) == csa2.OK
     assert lib.csa2_debug_dequant(7, None, None, 1, None, None) == csa2.ERR_INVALID_ARG
+
+
+def test_stream_read_validates_before_launch(lib):
+    assert lib.csa2_debug_stream_read(None, 0, None, None) == csa2.OK
+    assert lib.csa2_debug_stream_read(None, 15, None, None) == csa2.ERR_INVALID_ARG
+    assert lib.csa2_debug_stream_read(None, -16, None, None) == csa2.ERR_INVALID_ARG
+    assert lib.csa2_debug_stream_read(None, 16, None, None) == csa2.ERR_INVALID_ARG      # null source
+    assert lib.csa2_debug_stream_read(0x10008, 16, 0x20000, None) == csa2.ERR_INVALID_ARG  # misaligned
