@@ -68,6 +68,7 @@ struct ScanArgs {
   int64_t blk_ld;
   int32_t entry_tiles;    // workgroups of the entry part (grid.x after the block part)
   int32_t iters;          // 64-entry chunks per wave in the entry part
+  int32_t blk_groups;     // 16-summary groups per wave in the block part
   int32_t block_tiles;    // workgroups of the block part (first in grid.x)
   const int32_t* kept;    // candidate-only scan: [R][kept_ld]
   const int32_t* n_kept;

@@ -251,14 +251,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
   } else {
     int64_t bl0, nb;
     req_blocks(a.g, b, n, bl0, nb);
-    const int64_t base = (int64_t)blockIdx.x * kTile + wave * (kGroups * 16);
+    // 16 x bgroups summaries per wave.  A summary is 256 B (3.8x an entry's 68 B), so
+    // with one entry chunk per wave the block tiles take one group per wave and finish
+    // with the entry tiles; larger scans give them up to four.
+    const int bgroups = a.blk_groups;
+    const int64_t base = (int64_t)blockIdx.x * (kWaves * 16) * bgroups + wave * 16 * bgroups;
     if (base >= nb) return;
     bf16x8_t qa[MAXPAIRS][4];
     float wv[MAXPAIRS][4];
     load_query<MAXPAIRS>(a, r0, r1, qa, wv);
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-      int64_t j = base + gi * 16 + m;
+    for (int gi = 0; gi < bgroups; ++gi) {
+      const int64_t j = base + gi * 16 + m;
       const int64_t jl = j < nb ? j : nb - 1;
       const uint16_t* sp = a.blk_sum + (bl0 + jl) * CSA2_IDX_D + 32 * g;
       bf16x8_t kb[4];
@@ -335,7 +338,9 @@ hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool bloc
   while (iters < kMaxIters && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
   a.iters = iters;
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;
-  a.block_tiles = blocks ? (int32_t)((max_nb + kTile - 1) / kTile) : 0;
+  a.blk_groups = iters < kGroups ? iters : kGroups;
+  const int64_t blk_tile = (int64_t)kWaves * 16 * a.blk_groups;
+  a.block_tiles = blocks ? (int32_t)((max_nb + blk_tile - 1) / blk_tile) : 0;
   const int gx = a.entry_tiles + a.block_tiles;
   if (gx == 0 || a.g.B == 0 || a.g.R == 0) return hipSuccess;
   const dim3 grid(gx, a.g.B);
