@@ -102,6 +102,24 @@ def test_index_score_matches_oracle(csa2, rows):
             assert np.all(np.isnan(scores[r, n:])), "scores beyond the request's entries were written"
 
 
+@pytest.mark.parametrize("rows", [1, 3, 6, 16])
+def test_index_score_multi_chunk_waves(csa2, rows):
+    # Requests long enough that each wave walks several 64-entry chunks (the launch
+    # heuristic doubles chunks per wave at 4 x 262144 entries), with ragged tails, for
+    # every query-row grouping (score staging per workgroup and per chunk).
+    lens = [262144, 262144 - 37, 200001, 262144]
+    _log(f"index scan, multi-chunk waves: rows/request {rows}, lengths {lens}")
+    wl = make_workload("scanlong", 40 + rows, lens, rows_per_req=rows, n_needles=3, scan_only=True)
+    dw = upload(wl)
+    scores = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
+    for b in range(wl.num_requests):
+        ref = oracle.request_scores(wl, b)
+        n = wl.n_entries(b)
+        for j, r in enumerate(range(int(wl.row_off[b]), int(wl.row_off[b + 1]))):
+            _score_close(scores[r, :n], ref[j], f"request {b} row {r}")
+            assert np.all(np.isnan(scores[r, n:])), "scores beyond the request's entries were written"
+
+
 def test_block_filter_matches_oracle(csa2):
     lens = [64 * 64, 64 * 64 + 1, 64 * 100 + 17, 64 * 300, 5000, 10]
     _log(f"block filter: lengths {lens}")
@@ -223,6 +241,34 @@ def test_sparse_attn_matches_oracle(csa2, k, swa):
                                 torch.from_numpy(n_sel).cuda(), dw.swa, dw.swa_scale, wl.sm_scale)
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     for r in range(R):
+        ro, rl = oracle.joint_attention(oracle.bf16_value(wl.q[r]), oracle.row_keys(wl, r, sel[r, :n_sel[r]]),
+                                        wl.sm_scale)
+        rel, dl = parity.attn_error(out[r], lse[r], ro, rl)
+        assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS, f"row {r}: rel {rel:.3g} lse {dl:.3g}"
+
+
+def test_sparse_attn_many_rows_single_split(csa2):
+    # With enough rows each row's keys go to one workgroup, which normalises and writes
+    # the output itself (no split partials, no merge); some rows also span several tiles.
+    R, k = 272, 200
+    lens = [300 + 7 * b for b in range(R)]
+    _log(f"attention: {R} rows, k {k}, one split per row")
+    wl = make_workload("attnmany", 77, lens, rows_per_req=1, n_needles=0,
+                       swa_len=[128 if b % 5 else b % 128 for b in range(R)])
+    dw = upload(wl)
+    rng = np.random.default_rng(5)
+    sel = np.full((R, k), -1, dtype=np.int32)
+    n_sel = np.zeros(R, dtype=np.int32)
+    for r in range(R):
+        n = wl.n_entries(int(wl.row_req[r]))
+        m = min(k, n) - (r % 3)
+        sel[r, :m] = np.sort(rng.choice(n, size=m, replace=False))
+        n_sel[r] = m
+    assert csa2.sparse_attn_workspace_size(dw.rg, k) == 0, "expected the single-split plan"
+    out, lse = csa2.sparse_attn(dw.rg, dw.q, dw.main_kv, torch.from_numpy(sel).cuda(),
+                                torch.from_numpy(n_sel).cuda(), dw.swa, dw.swa_scale, wl.sm_scale)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for r in range(0, R, 3):
         ro, rl = oracle.joint_attention(oracle.bf16_value(wl.q[r]), oracle.row_keys(wl, r, sel[r, :n_sel[r]]),
                                         wl.sm_scale)
         rel, dl = parity.attn_error(out[r], lse[r], ro, rl)
