@@ -44,7 +44,13 @@
  *     (that would need a sync); kernels clamp offsets and lengths to the pool sizes and
  *     the host-side maxima given below, so inconsistent descriptors yield wrong results
  *     rather than out-of-bounds accesses.
- *   - Positions are request-local: entry t of request b is pool row entry_off[b] + t.
+ *   - Positions are request-local: entry t of request b is pool row entry_off[b] + t
+ *     (contiguous pools) or row 64*page_table[b*pages_ld + t/64] + t%64 (paged pools).
+ *   - Score check (SGLang blog, section "DSpark adaptation and optimization": the
+ *     post-top-k score check and invalid-position filter): an entry or block whose score
+ *     is NaN (e.g. an E8M0 scale byte of 255) is never ranked; block selection and top-k
+ *     run over the others.  NaN ranks below every number, so this equals ranking
+ *     everything and dropping NaN-scored picks afterwards.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -56,7 +62,7 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 1
+#define CSA2_VERSION 2
 
 /* Fixed dimensions. */
 #define CSA2_D           512   /* latent dim = attention K = V dim */
@@ -96,6 +102,23 @@ typedef struct csa2_ragged {
   int64_t total_blocks;           /* host: rows in the block-summary pool */
   int64_t swa_tokens;             /* host: rows in the window pool */
   int32_t max_rows_per_request;   /* host: >= max_b (row_off[b+1]-row_off[b]), <= 16 */
+  /* Per-row visible length (verify rows; SGLang blog, section "DSpark adaptation and
+   * optimization": the candidate mask carries each row's valid-length check).  NULL:
+   * every row sees all N_b entries of its request.  Otherwise row r sees entries
+   * 0 .. V_r-1, V_r = row_len[r] clamped to 0..N_b: its blocks are the first
+   * ceil(V_r/64) (the newest of them is block ceil(V_r/64)-1, possibly partial), only
+   * those entries are candidates, and attention skips selected positions >= V_r. */
+  const int64_t* row_len;         /* nullable device [R] */
+  /* Paged pools (same section: KV page-address translation).  NULL: contiguous pools as
+   * above.  Otherwise the idx_k / main_kv pools are made of 64-entry pages and the
+   * block-summary pool holds one summary per page: entry t of request b lives at pool
+   * row 64*p + t%64 and its block's summary at row p, p = page_table[b*pages_ld + t/64];
+   * entry_off then only gives the lengths N_b = entry_off[b+1] - entry_off[b], and
+   * block_off is unused (may be NULL).  Page ids are clamped to 0..total_pages-1. */
+  const int32_t* page_table;      /* nullable device [B][pages_ld] */
+  int32_t pages_ld;               /* host: >= ceil(max_entries/64) when page_table != NULL */
+  int64_t total_pages;            /* host: >= 1 when paged; 64*total_pages <= total_entries,
+                                     total_pages <= total_blocks */
 } csa2_ragged;
 
 /*

@@ -35,6 +35,20 @@ them (each is restated where it is used):
                    softmax jointly over the selected entries and the row's window,
                    logit scale 1/sqrt(512), no de-duplication, no sink.
 
+[SGL] "DSpark adaptation and optimization" also names a valid-length check fused into
+the candidate mask and a post-top-k step that checks scores, filters invalid positions
+and translates positions into KV page addresses.  Read here as:
+  * row visibility: a row may see only the first V_r entries of its request (verify
+                   rows sit at consecutive positions); the row then works on the request
+                   cut to V_r entries: blocks 0 .. ceil(V_r/64)-1, candidates < V_r;
+  * score check  : a NaN score (possible through an E8M0 NaN scale) is never ranked;
+                   since NaN would rank below every number, dropping NaN picks after the
+                   top-k gives the same set;
+  * invalid positions: selected positions outside 0 .. V_r-1 carry no key;
+  * pages        : the pools may be cut into 64-entry pages; entry t of request b is
+                   then at row 64 * page_table[b][t // 64] + t % 64 and its block's
+                   summary at row page_table[b][t // 64].
+
 Every function here is pinned by tests in tests/test_formats.py and tests/test_oracle.py
 (format tables against a library decoder and the OCP MX value table, brute-force exact
 rational scores, brute-force selection, the dense-attention special case, LSE merging
@@ -150,15 +164,18 @@ def indexer_score(q_idx: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndar
 def keep_blocks(block_scores: np.ndarray, n_keep: int = 64, keep_newest: bool = True) -> np.ndarray:
     """Blocks kept by the coarse stage, ascending.
 
-    With nb <= n_keep every block is kept.  Otherwise order blocks by (score desc,
-    block asc), keep the first n_keep, and add the newest block (nb-1) if it is not
-    among them.
+    Blocks with a NaN score are not ranked (score check).  With at most n_keep ranked
+    blocks all of them are kept; otherwise order them by (score desc, block asc) and keep
+    the first n_keep.  Then add the newest block (nb-1) if it is not among them.
     """
-    nb = int(block_scores.shape[0])
-    if nb <= n_keep:
-        return np.arange(nb, dtype=np.int64)
-    order = np.lexsort((np.arange(nb), -np.asarray(block_scores, dtype=np.float64)))
-    kept = set(int(j) for j in order[:n_keep])
+    bs = np.asarray(block_scores, dtype=np.float64)
+    nb = int(bs.shape[0])
+    ranked = np.flatnonzero(~np.isnan(bs))
+    if ranked.size <= n_keep:
+        kept = set(int(j) for j in ranked)
+    else:
+        order = np.lexsort((ranked, -bs[ranked]))
+        kept = set(int(j) for j in ranked[order[:n_keep]])
     if keep_newest and nb > 0:
         kept.add(nb - 1)
     return np.array(sorted(kept), dtype=np.int64)
@@ -175,9 +192,13 @@ def blocks_to_entries(kept: np.ndarray, n_entries: int) -> np.ndarray:
 # ---------------------------------------------------------------------------------
 
 def top_k(positions: np.ndarray, scores: np.ndarray, k: int) -> np.ndarray:
-    """The k best (score desc, position asc) of the candidates, reported ascending."""
+    """The k best (score desc, position asc) of the candidates whose score is not NaN,
+    reported ascending."""
     positions = np.asarray(positions, dtype=np.int64)
-    order = np.lexsort((positions, -np.asarray(scores, dtype=np.float64)))
+    scores = np.asarray(scores, dtype=np.float64)
+    ok = ~np.isnan(scores)
+    positions, scores = positions[ok], scores[ok]
+    order = np.lexsort((positions, -scores))
     return np.sort(positions[order[:k]])
 
 
@@ -207,31 +228,62 @@ def joint_attention(q: np.ndarray, keys: np.ndarray, sm_scale: float) -> tuple[n
 # The whole path for one workload.
 # ---------------------------------------------------------------------------------
 
+def entry_rows(wl, b: int, t: np.ndarray) -> np.ndarray:
+    """Pool rows of entries ``t`` of request b: entry_off[b] + t, or with a page table
+    64 * page_table[b][t // 64] + t % 64."""
+    t = np.asarray(t, dtype=np.int64)
+    pt = getattr(wl, "page_table", None)
+    if pt is None:
+        return int(wl.entry_off[b]) + t
+    return np.asarray(pt[b], dtype=np.int64)[t // BLOCK] * BLOCK + t % BLOCK
+
+
+def block_rows(wl, b: int, nb: int) -> np.ndarray:
+    """Summary-pool rows of blocks 0 .. nb-1 of request b."""
+    j = np.arange(nb, dtype=np.int64)
+    pt = getattr(wl, "page_table", None)
+    if pt is None:
+        return int(wl.block_off[b]) + j
+    return np.asarray(pt[b], dtype=np.int64)[j]
+
+
+def visible(wl, r: int) -> int:
+    """Entries row r sees: N_b, or its row length clamped to 0 .. N_b."""
+    b = int(wl.row_req[r])
+    n = int(wl.entry_off[b + 1] - wl.entry_off[b])
+    rl = getattr(wl, "row_len", None)
+    return n if rl is None else min(max(int(rl[r]), 0), n)
+
+
 def request_scores(wl, b: int) -> np.ndarray:
     """Index scores of every entry of request b for each of its rows: [rows_b, N_b]."""
     r0, r1 = int(wl.row_off[b]), int(wl.row_off[b + 1])
-    e0, e1 = int(wl.entry_off[b]), int(wl.entry_off[b + 1])
-    out = np.zeros((r1 - r0, e1 - e0), dtype=np.float64)
+    n = int(wl.entry_off[b + 1] - wl.entry_off[b])
+    out = np.zeros((r1 - r0, n), dtype=np.float64)
     qs = [bf16_value(wl.q_idx[r]) for r in range(r0, r1)]
-    for c0 in range(e0, e1, SCAN_CHUNK):
-        c1 = min(e1, c0 + SCAN_CHUNK)
-        keys = dequant_idx(wl.idx_k[c0:c1])
+    for c0 in range(0, n, SCAN_CHUNK):
+        c1 = min(n, c0 + SCAN_CHUNK)
+        keys = dequant_idx(wl.idx_k[entry_rows(wl, b, np.arange(c0, c1))])
         for j, r in enumerate(range(r0, r1)):
-            out[j, c0 - e0:c1 - e0] = indexer_score(qs[j], wl.w[r], keys)
+            out[j, c0:c1] = indexer_score(qs[j], wl.w[r], keys)
     return out
 
 
 def block_scores_row(wl, r: int) -> np.ndarray:
+    """Scores of the blocks row r sees (ceil(V_r / 64) of them)."""
     b = int(wl.row_req[r])
-    summ = bf16_value(wl.blk_sum[int(wl.block_off[b]):int(wl.block_off[b + 1])])
+    nb = -(-visible(wl, r) // BLOCK)
+    summ = bf16_value(wl.blk_sum[block_rows(wl, b, nb)])
     return indexer_score(bf16_value(wl.q_idx[r]), wl.w[r], summ)
 
 
 def row_keys(wl, r: int, sel: np.ndarray) -> np.ndarray:
-    """The row's attention keys: the selected main entries, then its window tokens."""
+    """The row's attention keys: the selected main entries that are valid positions
+    (0 .. V_r-1; others carry no key), then its window tokens."""
     b = int(wl.row_req[r])
-    e0 = int(wl.entry_off[b])
-    main = dequant_main(wl.main_kv[e0 + np.asarray(sel, dtype=np.int64)])
+    sel = np.asarray(sel, dtype=np.int64)
+    sel = sel[(sel >= 0) & (sel < visible(wl, r))]
+    main = dequant_main(wl.main_kv[entry_rows(wl, b, sel)])
     s0 = int(wl.row_swa_start[r])
     s1 = s0 + int(wl.row_swa_len[r])
     win = dequant_swa(wl.swa[s0:s1], wl.swa_scale[s0:s1])
@@ -267,7 +319,7 @@ def decode(wl, rows=None, k: int | None = None, n_keep: int | None = None, keep_
                 kept = np.asarray(kept_override[r], dtype=np.int64)
             else:
                 kept = keep_blocks(bs, n_keep, bool(keep_newest))
-            cand = blocks_to_entries(kept, n)
+            cand = blocks_to_entries(kept, visible(wl, r))
             cs = s[cand]
             if sel_override is not None and r in sel_override:
                 sel = np.asarray(sel_override[r], dtype=np.int64)

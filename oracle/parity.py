@@ -23,16 +23,19 @@ LSE_ABS = 2e-3
 
 
 def kth_best(scores: np.ndarray, k: int) -> float:
-    if scores.size == 0:
+    """k-th best of the scores that are not NaN (NaN scores are never ranked)."""
+    s = np.asarray(scores, dtype=np.float64)
+    s = s[~np.isnan(s)]
+    if s.size == 0:
         return 0.0
-    k = min(k, scores.size)
-    return float(np.sort(np.asarray(scores, dtype=np.float64))[::-1][k - 1])
+    k = min(k, s.size)
+    return float(np.sort(s)[::-1][k - 1])
 
 
 def band_ok(diff_positions, score_of, boundary: float, rel: float) -> tuple[bool, str]:
     for t in diff_positions:
         s = float(score_of(t))
-        if abs(s - boundary) > rel * abs(boundary):
+        if np.isnan(s) or abs(s - boundary) > rel * abs(boundary):
             return False, f"position {t} (score {s!r}) differs but is outside the band around {boundary!r}"
     return True, ""
 
@@ -57,8 +60,7 @@ def check_row(wl, r: int, ref: dict, kept_gpu: np.ndarray | None, sel_gpu: np.nd
     k = wl.k if k is None else k
     n_keep = wl.n_keep if n_keep is None else n_keep
     rep = {"row": r, "ok": True, "msgs": []}
-    b = int(wl.row_req[r])
-    n = int(wl.entry_off[b + 1] - wl.entry_off[b])
+    n = O.visible(wl, r)
 
     # Coarse stage.
     kept_ref = ref["kept"]
@@ -87,7 +89,7 @@ def check_row(wl, r: int, ref: dict, kept_gpu: np.ndarray | None, sel_gpu: np.nd
         rep["msgs"].append("selected positions are not strictly ascending")
     if not rep["set_equal"]:
         boundary = kth_best(cs, k)
-        score_of = dict(zip(cand.tolist(), cs.tolist()))
+        score_of = {t: v for t, v in zip(cand.tolist(), cs.tolist()) if not np.isnan(v)}
         diff = set(sel_gpu.tolist()) ^ set(sel_ref.tolist())
         outside = [t for t in diff if t not in score_of]
         if outside:

@@ -40,6 +40,8 @@ class _Ragged(ctypes.Structure):
         ("row_req", ctypes.c_void_p), ("row_swa_start", ctypes.c_void_p), ("row_swa_len", ctypes.c_void_p),
         ("max_entries", ctypes.c_int64), ("total_entries", ctypes.c_int64), ("total_blocks", ctypes.c_int64),
         ("swa_tokens", ctypes.c_int64), ("max_rows_per_request", ctypes.c_int32),
+        ("row_len", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("pages_ld", ctypes.c_int32),
+        ("total_pages", ctypes.c_int64),
     ]
 
 
@@ -130,9 +132,13 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 @dataclass
 class Ragged:
-    """Ragged batch descriptor: device offset tensors plus host maxima (see csa2.h)."""
+    """Ragged batch descriptor: device offset tensors plus host maxima (see csa2.h).
+
+    Optional: ``row_len`` (int64 [R], entries each row sees) and ``page_table`` (int32
+    [B][pages_ld], paged pools of 64-entry pages, ``total_pages`` of them; then
+    ``block_off`` may be None)."""
     entry_off: torch.Tensor       # int64 [B+1]
-    block_off: torch.Tensor       # int64 [B+1]
+    block_off: torch.Tensor | None  # int64 [B+1]
     row_off: torch.Tensor         # int32 [B+1]
     row_req: torch.Tensor         # int32 [R]
     row_swa_start: torch.Tensor   # int64 [R]
@@ -142,6 +148,9 @@ class Ragged:
     total_blocks: int
     swa_tokens: int
     max_rows_per_request: int
+    row_len: torch.Tensor | None = None      # int64 [R]
+    page_table: torch.Tensor | None = None   # int32 [B][pages_ld]
+    total_pages: int = 0
 
     @property
     def num_requests(self) -> int:
@@ -153,12 +162,18 @@ class Ragged:
 
     def c(self) -> _Ragged:
         for name, dt in (("entry_off", torch.int64), ("block_off", torch.int64), ("row_off", torch.int32),
-                         ("row_req", torch.int32), ("row_swa_start", torch.int64), ("row_swa_len", torch.int32)):
-            _dev(getattr(self, name), (dt,), name)
+                         ("row_req", torch.int32), ("row_swa_start", torch.int64), ("row_swa_len", torch.int32),
+                         ("row_len", torch.int64), ("page_table", torch.int32)):
+            if getattr(self, name) is not None:
+                _dev(getattr(self, name), (dt,), name)
+        pt = self.page_table
+        if pt is not None and (pt.dim() != 2 or pt.shape[0] != self.num_requests):
+            raise ValueError("page_table must be [num_requests][pages_ld]")
         return _Ragged(self.num_requests, self.num_rows, _ptr(self.entry_off), _ptr(self.block_off),
                        _ptr(self.row_off), _ptr(self.row_req), _ptr(self.row_swa_start), _ptr(self.row_swa_len),
                        int(self.max_entries), int(self.total_entries), int(self.total_blocks), int(self.swa_tokens),
-                       int(self.max_rows_per_request))
+                       int(self.max_rows_per_request), _ptr(self.row_len), _ptr(pt),
+                       int(pt.shape[1]) if pt is not None else 0, int(self.total_pages))
 
 
 def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:

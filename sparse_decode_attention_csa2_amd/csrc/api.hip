@@ -36,8 +36,10 @@ int check_ragged(const csa2_ragged* rg, RaggedDev& g) {
   if (rg->num_requests > 65535 || rg->num_rows > 65535)
     return fail(CSA2_ERR_UNSUPPORTED, "at most 65535 requests and 65535 rows per call");
   if (rg->num_rows > 0 && rg->num_requests == 0) return fail(CSA2_ERR_INVALID_ARG, "rows without requests");
-  if (rg->num_requests > 0 && (!rg->entry_off || !rg->block_off || !rg->row_off))
-    return fail(CSA2_ERR_INVALID_ARG, "entry_off/block_off/row_off is NULL");
+  if (rg->num_requests > 0 && (!rg->entry_off || !rg->row_off))
+    return fail(CSA2_ERR_INVALID_ARG, "entry_off/row_off is NULL");
+  if (rg->num_requests > 0 && !rg->page_table && !rg->block_off)
+    return fail(CSA2_ERR_INVALID_ARG, "block_off is NULL (required for contiguous pools)");
   if (rg->num_rows > 0 && (!rg->row_req || !rg->row_swa_start || !rg->row_swa_len))
     return fail(CSA2_ERR_INVALID_ARG, "row_req/row_swa_start/row_swa_len is NULL");
   if (rg->max_entries < 0 || rg->total_entries < 0 || rg->total_blocks < 0 || rg->swa_tokens < 0)
@@ -46,20 +48,36 @@ int check_ragged(const csa2_ragged* rg, RaggedDev& g) {
     return fail(CSA2_ERR_INVALID_ARG, "max_entries %lld exceeds total_entries %lld", (long long)rg->max_entries,
                 (long long)rg->total_entries);
   if (rg->max_entries >= (int64_t(1) << 31)) return fail(CSA2_ERR_UNSUPPORTED, "max_entries must be < 2^31");
+  if (rg->total_blocks >= (int64_t(1) << 31) || rg->swa_tokens >= (int64_t(1) << 31))
+    return fail(CSA2_ERR_UNSUPPORTED, "total_blocks and swa_tokens must be < 2^31");
   if (rg->num_rows > 0 && (rg->max_rows_per_request < 1 || rg->max_rows_per_request > CSA2_ROWS_PER_REQ_MAX))
     return fail(CSA2_ERR_UNSUPPORTED, "max_rows_per_request must be in 1..%d", CSA2_ROWS_PER_REQ_MAX);
+  if (rg->page_table) {
+    if (rg->pages_ld < ceil_div(rg->max_entries, CSA2_BLOCK) || rg->pages_ld < 1)
+      return fail(CSA2_ERR_INVALID_ARG, "pages_ld %d < ceil(max_entries/64)", rg->pages_ld);
+    if (rg->total_pages < 1) return fail(CSA2_ERR_INVALID_ARG, "paged pools need total_pages >= 1");
+    if (rg->total_pages > rg->total_blocks || rg->total_pages > rg->total_entries / CSA2_BLOCK)
+      return fail(CSA2_ERR_INVALID_ARG, "total_pages %lld exceeds the pools (%lld entries, %lld summaries)",
+                  (long long)rg->total_pages, (long long)rg->total_entries, (long long)rg->total_blocks);
+    if (rg->total_pages >= (int64_t(1) << 31) / CSA2_BLOCK)
+      return fail(CSA2_ERR_UNSUPPORTED, "paged pools must hold fewer than 2^31 entries");
+  }
   g.entry_off = rg->entry_off;
   g.block_off = rg->block_off;
   g.row_off = rg->row_off;
   g.row_req = rg->row_req;
   g.row_swa_start = rg->row_swa_start;
   g.row_swa_len = rg->row_swa_len;
-  g.max_entries = rg->max_entries;
+  g.max_entries = (int32_t)rg->max_entries;
   g.total_entries = rg->total_entries;
-  g.total_blocks = rg->total_blocks;
-  g.swa_tokens = rg->swa_tokens;
+  g.total_blocks = (int32_t)rg->total_blocks;
+  g.swa_tokens = (int32_t)rg->swa_tokens;
   g.B = rg->num_requests;
   g.R = rg->num_rows;
+  g.row_len = rg->row_len;
+  g.page_table = rg->page_table;
+  g.pages_ld = rg->page_table ? rg->pages_ld : 0;
+  g.total_pages = rg->page_table ? (int32_t)rg->total_pages : 0;
   return CSA2_OK;
 }
 
@@ -274,9 +292,13 @@ int csa2_topk(const csa2_ragged* rg, const float* scores, int64_t ld, const int3
   return CSA2_OK;
 }
 
+// Standalone attention workspace: the split partials, then (paged pools) the selected
+// positions translated to pool rows.
 size_t csa2_sparse_attn_workspace_size(const csa2_ragged* rg, int32_t sel_ld) {
   if (!rg || rg->num_rows <= 0 || sel_ld < 1) return 0;
-  return attn_workspace_bytes(rg->num_rows, sel_ld);
+  size_t n = round_up(attn_workspace_bytes(rg->num_rows, sel_ld), 256);
+  if (rg->page_table) n += round_up((size_t)rg->num_rows * sel_ld * sizeof(int32_t), 256);
+  return n;
 }
 
 static int attn_args(const RaggedDev& g, const uint16_t* q, const uint8_t* main_kv, const int32_t* sel_idx,
@@ -326,16 +348,34 @@ int csa2_sparse_attn(const csa2_ragged* rg, const uint16_t* q, const uint8_t* ma
   RaggedDev g;
   CHECK(check_ragged(rg, g));
   if (g.R == 0) return CSA2_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   AttnArgs a{};
-  CHECK(attn_args(g, q, main_kv, sel_idx, n_sel, sel_ld, swa, swa_scale, sm_scale, out, lse, ws, ws_bytes, a));
-  LAUNCH(launch_attn(a, reinterpret_cast<hipStream_t>(stream)), "sparse attention");
+  if (!g.page_table) {
+    CHECK(attn_args(g, q, main_kv, sel_idx, n_sel, sel_ld, swa, swa_scale, sm_scale, out, lse, ws, ws_bytes, a));
+    LAUNCH(launch_attn(a, st), "sparse attention");
+    return CSA2_OK;
+  }
+  // Paged pools: translate the positions to pool rows first.
+  CHECK(check_ptr(sel_idx, 4, "sel_idx"));
+  CHECK(check_ptr(n_sel, 4, "n_sel"));
+  if (sel_ld < 1 || sel_ld > CSA2_K_MAX) return fail(CSA2_ERR_UNSUPPORTED, "sel_ld must be in 1..%d", CSA2_K_MAX);
+  const size_t need = csa2_sparse_attn_workspace_size(rg, sel_ld);
+  if (!ws || ws_bytes < need)
+    return fail(CSA2_ERR_WORKSPACE_TOO_SMALL, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(CSA2_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int32_t* rows = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                             round_up(attn_workspace_bytes(g.R, sel_ld), 256));
+  CHECK(attn_args(g, q, main_kv, rows, n_sel, sel_ld, swa, swa_scale, sm_scale, out, lse, ws, ws_bytes, a));
+  a.sel_rows = 1;
+  LAUNCH(launch_sel_rows(g, sel_idx, n_sel, sel_ld, rows, st), "position translation");
+  LAUNCH(launch_attn(a, st), "sparse attention");
   return CSA2_OK;
 }
 
 // Workspace of csa2_decode, in carve order.
 static size_t decode_layout(const csa2_decode_args* a, char* base, float** scores, float** blk_scores,
-                            int32_t** kept, int32_t** n_kept, int32_t** sel, int32_t** n_sel, char** attn_ws,
-                            size_t* attn_bytes) {
+                            int32_t** kept, int32_t** n_kept, int32_t** sel, int32_t** n_sel, int32_t** sel_rows,
+                            char** attn_ws, size_t* attn_bytes) {
   const csa2_ragged& rg = a->rg;
   const int64_t R = rg.num_rows;
   const int64_t ld = round_up((size_t)(rg.max_entries > 0 ? rg.max_entries : 1), 64);
@@ -353,6 +393,8 @@ static size_t decode_layout(const csa2_decode_args* a, char* base, float** score
   if (sel) *sel = a->sel_idx ? a->sel_idx : sl;
   int32_t* ns = a->n_sel ? nullptr : c.take<int32_t>((size_t)R);
   if (n_sel) *n_sel = a->n_sel ? a->n_sel : ns;
+  int32_t* sr = rg.page_table ? c.take<int32_t>((size_t)R * a->k) : nullptr;
+  if (sel_rows) *sel_rows = sr;
   const size_t ab = attn_workspace_bytes(R, a->k);
   char* aw = c.take<char>(ab);
   if (attn_ws) *attn_ws = aw;
@@ -362,7 +404,7 @@ static size_t decode_layout(const csa2_decode_args* a, char* base, float** score
 
 size_t csa2_decode_workspace_size(const csa2_decode_args* a) {
   if (!a || a->rg.num_rows <= 0 || a->k < 1 || a->n_keep < 1) return 0;
-  return decode_layout(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return decode_layout(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
@@ -389,16 +431,20 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   if (!aligned(ws, 256)) return fail(CSA2_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
   float *scores, *blk_scores;
-  int32_t *kept, *n_kept, *sel, *n_sel;
+  int32_t *kept, *n_kept, *sel, *n_sel, *sel_rows;
   char* attn_ws;
   size_t attn_bytes;
-  decode_layout(a, static_cast<char*>(ws), &scores, &blk_scores, &kept, &n_kept, &sel, &n_sel, &attn_ws, &attn_bytes);
+  decode_layout(a, static_cast<char*>(ws), &scores, &blk_scores, &kept, &n_kept, &sel, &n_sel, &sel_rows, &attn_ws,
+                &attn_bytes);
   const int64_t ld = a->scores ? a->scores_ld : (int64_t)round_up((size_t)(g.max_entries > 0 ? g.max_entries : 1), 64);
   const int64_t blk_ld = (int64_t)round_up((size_t)(blocks_of(g.max_entries) > 0 ? blocks_of(g.max_entries) : 1), 64);
 
+  // Paged pools: the fine top-k also writes the picks' pool rows (translation fused into
+  // the selection), and attention reads those.
   AttnArgs at{};
-  CHECK(attn_args(g, a->q, a->main_kv, sel, n_sel, a->k, a->swa, a->swa_scale, a->sm_scale, a->out, a->lse, attn_ws,
-                  attn_bytes, at));
+  CHECK(attn_args(g, a->q, a->main_kv, sel_rows ? sel_rows : sel, n_sel, a->k, a->swa, a->swa_scale, a->sm_scale,
+                  a->out, a->lse, attn_ws, attn_bytes, at));
+  at.sel_rows = sel_rows ? 1 : 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   ScanArgs sa{};
@@ -426,6 +472,7 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   se.k = a->k;
   se.sel = sel;
   se.n_sel = n_sel;
+  se.sel_rows = sel_rows;
 
   auto mark = [&](int i) -> hipError_t {
     return a->events ? hipEventRecord(static_cast<hipEvent_t>(a->events[i]), st) : hipSuccess;

@@ -35,7 +35,8 @@ constexpr int kAttnTileKeys = 64;
 #endif
 
 struct RowKeys {
-  int64_t e0, n;     // request's first pool entry and entry count
+  int64_t e0, n;     // pool row of position 0 and the positions the row sees (pool rows
+                     // themselves, 0 .. total_entries-1, when sel holds pool rows)
   int n_main;        // selected main entries (slots)
   int64_t s0;        // first window token
   int n_swa;
@@ -43,8 +44,13 @@ struct RowKeys {
 
 __device__ __forceinline__ RowKeys row_keys(const AttnArgs& a, int r) {
   RowKeys k;
+  const int64_t vis = row_len_raw(a.g, r);
   const int b = row_request(a.g, r);
-  req_entries(a.g, b, k.e0, k.n);
+  int64_t e0, n;
+  req_entries(a.g, b, e0, n);
+  n = row_visible(a.g, vis, n);
+  k.e0 = a.sel_rows ? 0 : e0;
+  k.n = a.sel_rows ? a.g.total_entries : n;
   int ns = a.n_sel[r];
   k.n_main = ns < 0 ? 0 : (ns > a.sel_ld ? a.sel_ld : ns);
   int64_t s0 = a.g.row_swa_start[r];
@@ -341,6 +347,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 constexpr int kMaxSplits = (CSA2_K_MAX + CSA2_SWA_MAX + 31) / 32;
 
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  touch_kernargs<sizeof(AttnArgs)>();
   __shared__ float msh[kMaxSplits][16], lsh[kMaxSplits][16];
   const int r = blockIdx.y, w = blockIdx.x >> 3, tg = blockIdx.x & 7;
   const RowKeys rk = row_keys(a, r);
@@ -426,6 +433,30 @@ hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0 || a.splits == 1) return hipSuccess;
   k_attn_merge<<<dim3(32, a.g.R), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// Selected positions -> pool rows, one thread per slot.
+__global__ __launch_bounds__(256) void k_sel_rows(RaggedDev g, const int32_t* sel, const int32_t* n_sel,
+                                                 int32_t sel_ld, int32_t* rows) {
+  const int r = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= sel_ld) return;
+  int ns = n_sel[r];
+  ns = ns < 0 ? 0 : (ns > sel_ld ? sel_ld : ns);
+  const int64_t vis = row_len_raw(g, r);
+  const int b = row_request(g, r);
+  int64_t e0, n;
+  req_entries(g, b, e0, n);
+  n = row_visible(g, vis, n);
+  const int64_t pos = sel[(int64_t)r * sel_ld + i];
+  rows[(int64_t)r * sel_ld + i] = (i < ns && pos >= 0 && pos < n) ? (int32_t)entry_row(g, b, e0, pos) : -1;
+}
+
+hipError_t launch_sel_rows(const RaggedDev& g, const int32_t* sel, const int32_t* n_sel, int32_t sel_ld,
+                           int32_t* rows, hipStream_t st) {
+  if (g.R == 0) return hipSuccess;
+  k_sel_rows<<<dim3((sel_ld + 255) / 256, g.R), dim3(256), 0, st>>>(g, sel, n_sel, sel_ld, rows);
   return hipGetLastError();
 }
 

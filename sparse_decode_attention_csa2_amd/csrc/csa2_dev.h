@@ -104,12 +104,14 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 }
 
 // ---------------------------------------------------------------------------------
-// Selection keys: larger score -> larger unsigned key; +0 and -0 map to one key.
+// Selection keys: larger score -> larger unsigned key; +0 and -0 map to one key; NaN
+// maps to 0, the key of an empty item (a NaN score never takes part in a ranking).
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return s != s ? 0u : key;
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
@@ -181,6 +183,28 @@ __device__ __forceinline__ T block_excl_scan(T v, T* tmp, T& total) {
 
 __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
+}
+
+#ifndef CSA2_TOUCH_KERNARGS
+#define CSA2_TOUCH_KERNARGS 1
+#endif
+
+// Reads one dword of each 64-byte line of the first BYTES of the kernel's argument
+// segment, all in the kernel's first round of scalar loads.  A kernel's arguments are
+// otherwise fetched as it needs them, and a line first touched after a dependent load
+// costs another full memory round trip on the kernel's critical path.
+template <int BYTES>
+__device__ __forceinline__ void touch_kernargs() {
+#if CSA2_TOUCH_KERNARGS
+  static_assert(BYTES <= 256, "at most four argument lines");
+  const uint32_t __attribute__((address_space(4)))* p =
+      (const uint32_t __attribute__((address_space(4)))*)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t v0 = p[0];
+  const uint32_t v1 = BYTES > 64 ? p[16] : 0u;
+  const uint32_t v2 = BYTES > 128 ? p[32] : 0u;
+  const uint32_t v3 = BYTES > 192 ? p[48] : 0u;
+  asm volatile("" ::"s"(v0), "s"(v1), "s"(v2), "s"(v3));
+#endif
 }
 
 }  // namespace csa2

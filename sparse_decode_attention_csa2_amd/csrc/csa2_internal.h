@@ -7,6 +7,8 @@ namespace csa2 {
 
 // The ragged descriptor as the kernels see it: device offset arrays plus host maxima
 // used both for grid sizing and to clamp every device-provided offset.
+// Every kernel receives it by value, so it is kept small (the host checks that the
+// counts held in 32 bits fit).
 struct RaggedDev {
   const int64_t* entry_off;
   const int64_t* block_off;
@@ -14,27 +16,77 @@ struct RaggedDev {
   const int32_t* row_req;
   const int64_t* row_swa_start;
   const int32_t* row_swa_len;
-  int64_t max_entries;
+  const int64_t* row_len;      // nullable [R]: entries visible to each row
+  const int32_t* page_table;   // nullable [B][pages_ld]: paged pools
   int64_t total_entries;
-  int64_t total_blocks;
-  int64_t swa_tokens;
+  int32_t max_entries;
+  int32_t total_blocks;
+  int32_t swa_tokens;
+  int32_t total_pages;
+  int32_t pages_ld;
   int32_t B;
   int32_t R;
 };
 
-// Entries of request b, clamped to the pool and to max_entries.
-__device__ __forceinline__ void req_entries(const RaggedDev& g, int b, int64_t& e0, int64_t& n) {
-  const int64_t a = clamp64(g.entry_off[b], 0, g.total_entries);
-  const int64_t z = clamp64(g.entry_off[b + 1], a, g.total_entries);
-  e0 = a;
+__device__ __forceinline__ bool paged(const RaggedDev& g) { return g.page_table != nullptr; }
+
+// Entries of request b, clamped to max_entries and (contiguous pools) to the pool; e0
+// is the first pool row (contiguous pools only; 0 when paged).  Branch-free, so the
+// loads issue together with the caller's other start-up loads.
+// Kernels instantiated per pool layout pass `pg` as a constant; the default reads the
+// descriptor.
+__device__ __forceinline__ void req_entries(const RaggedDev& g, int b, int64_t& e0, int64_t& n, bool pg) {
+  const int64_t a0 = g.entry_off[b], z0 = g.entry_off[b + 1];
+  const int64_t a = pg ? a0 : clamp64(a0, 0, g.total_entries);
+  const int64_t z = pg ? (z0 < a ? a : z0) : clamp64(z0, a, g.total_entries);
+  e0 = pg ? 0 : a;
   n = (z - a) < g.max_entries ? (z - a) : g.max_entries;
 }
+__device__ __forceinline__ void req_entries(const RaggedDev& g, int b, int64_t& e0, int64_t& n) {
+  req_entries(g, b, e0, n, paged(g));
+}
 
-// First summary of request b and how many of its ceil(n/64) summaries the pool holds.
-__device__ __forceinline__ void req_blocks(const RaggedDev& g, int b, int64_t n, int64_t& bl0, int64_t& nb_avail) {
-  bl0 = clamp64(g.block_off[b], 0, g.total_blocks);
+// Entries row r sees out of its request's n, in two steps: row_len_raw loads the row's
+// value (unconditionally, from a valid address either way, and before anything that
+// depends on the request, so that it joins the first round of loads), row_visible
+// applies it.
+__device__ __forceinline__ int64_t row_len_raw(const RaggedDev& g, int r) {
+  return *(g.row_len ? g.row_len + r : g.entry_off);
+}
+__device__ __forceinline__ int64_t row_visible(const RaggedDev& g, int64_t raw, int64_t n) {
+  return g.row_len ? clamp64(raw, 0, n) : n;
+}
+
+// Physical page of logical page (block) j of request b; j < ceil(max_entries/64) <=
+// pages_ld is the caller's to ensure.
+__device__ __forceinline__ int64_t page_of(const RaggedDev& g, int b, int64_t j) {
+  const int p = g.page_table[(int64_t)b * g.pages_ld + j];
+  return p < 0 ? 0 : (p >= g.total_pages ? g.total_pages - 1 : p);
+}
+
+// First summary of request b and how many of its ceil(n/64) summaries the pool holds
+// (paged pools: bl0 is unused and every summary is addressed through its page).
+__device__ __forceinline__ void req_blocks(const RaggedDev& g, int b, int64_t n, int64_t& bl0, int64_t& nb_avail,
+                                           bool pg) {
   const int64_t nb = (n + CSA2_BLOCK - 1) / CSA2_BLOCK;
+  if (pg) {
+    bl0 = 0;
+    nb_avail = nb;
+    return;
+  }
+  bl0 = clamp64(g.block_off[b], 0, g.total_blocks);
   nb_avail = (g.total_blocks - bl0) < nb ? (g.total_blocks - bl0) : nb;
+}
+__device__ __forceinline__ void req_blocks(const RaggedDev& g, int b, int64_t n, int64_t& bl0, int64_t& nb_avail) {
+  req_blocks(g, b, n, bl0, nb_avail, paged(g));
+}
+
+// Pool row of entry t (< n) of request b, and of the summary of its block j.
+__device__ __forceinline__ int64_t entry_row(const RaggedDev& g, int b, int64_t e0, int64_t t) {
+  return paged(g) ? page_of(g, b, t / CSA2_BLOCK) * CSA2_BLOCK + (t % CSA2_BLOCK) : e0 + t;
+}
+__device__ __forceinline__ int64_t block_row(const RaggedDev& g, int b, int64_t bl0, int64_t j) {
+  return paged(g) ? page_of(g, b, j) : bl0 + j;
 }
 
 // Rows of request b, clamped to [0, R) and to at most `cap` rows.
@@ -93,6 +145,7 @@ struct SelectArgs {
   int32_t* sel;              // [R][k]
   int32_t* n_sel;            // [R]
   float* sel_score;          // nullable [R][k]
+  int32_t* sel_rows;         // nullable [R][k]: pool rows of the selected entries (-1 pad)
 };
 
 hipError_t launch_block_select(SelectArgs a, hipStream_t st);
@@ -103,9 +156,10 @@ struct AttnArgs {
   RaggedDev g;
   const uint16_t* q;
   const uint8_t* main_kv;
-  const int32_t* sel;
+  const int32_t* sel;        // request-local positions, or pool rows when sel_rows != 0
   const int32_t* n_sel;
   int32_t sel_ld;
+  int32_t sel_rows;
   const uint8_t* swa;
   const float* swa_scale;
   float sm_scale_log2;       // sm_scale * log2(e)
@@ -124,6 +178,10 @@ size_t attn_workspace_bytes(int64_t R, int32_t sel_ld);
 hipError_t launch_attn(AttnArgs a, hipStream_t st);
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
+// Request-local selected positions -> pool rows (-1 for empty slots and positions the
+// row does not see), for attention over paged pools.
+hipError_t launch_sel_rows(const RaggedDev& g, const int32_t* sel, const int32_t* n_sel, int32_t sel_ld,
+                           int32_t* rows, hipStream_t st);
 
 hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
                                 hipStream_t st);

@@ -127,12 +127,13 @@ __device__ __forceinline__ void flush_chunk(float (*sb)[64], int nrows, int r0, 
 }
 
 // PARTS: 1 = entries only, 2 = block summaries only, 3 = both in one launch (distinct
-// instantiations keep the variants apart in kernel traces).
-template <int MAXPAIRS, int PARTS>
+// instantiations keep the variants apart in kernel traces).  PAGED: the pools are
+// 64-entry pages reached through the page table (a chunk is exactly one page).
+template <int MAXPAIRS, int PARTS, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS == 1 ? CSA2_SCAN_WAVES_PER_EU : (MAXPAIRS == 8 ? 1 : 2)))) void k_scan(ScanArgs a) {
   const int b = blockIdx.y;
   int64_t e0, n;
-  req_entries(a.g, b, e0, n);
+  req_entries(a.g, b, e0, n, PAGED);
   int r0, r1;
   req_rows(a.g, b, 2 * MAXPAIRS, r0, r1);
   if (r1 <= r0) return;
@@ -159,16 +160,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.idx_k + (e0 + wg_base) * CSA2_IDX_BYTES), (short)0, wg_n * CSA2_IDX_BYTES, kRsrcWord3);
     const int voff_c = m * CSA2_IDX_BYTES + 16 * g, voff_s = m * CSA2_IDX_BYTES + 64 + g;
+    // Paged pools: lane c holds the page of the wave's chunk c (logical page
+    // (wg_base + 64 wave)/64 + 4c); each chunk then gets a descriptor over its own page,
+    // limited to the entries the request has there.
+    int pv = 0;
+    if constexpr (PAGED) {
+      const int64_t lp = (wg_base + (int64_t)wave * 64) / CSA2_BLOCK + 4 * lane;
+      if (lane < a.iters && lp * CSA2_BLOCK < n) pv = (int)page_of(a.g, b, lp);
+    }
     struct Chunk {
       u32x4_t kc[kGroups];
       uint32_t ks[kGroups];
     };
     auto issue = [&](Chunk& ck, int lb) {
-      const int so = lb * CSA2_IDX_BYTES;
+      __amdgpu_buffer_rsrc_t r = rs;
+      int so = lb * CSA2_IDX_BYTES;
+      if constexpr (PAGED) {
+        const int c = (lb - wave * 64) / (kWaves * 64);   // the wave's chunk index (uniform)
+        const int64_t page = __builtin_amdgcn_readlane(pv, c);
+        const int cnt = min(64, wg_n - lb);
+        r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.idx_k + page * (CSA2_BLOCK * CSA2_IDX_BYTES)),
+                                              (short)0, cnt * CSA2_IDX_BYTES, kRsrcWord3);
+        so = 0;
+      }
 #pragma unroll
       for (int gi = 0; gi < kGroups; ++gi) {
-        ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_c + gi * 16 * CSA2_IDX_BYTES, so, 0);
-        ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff_s + gi * 16 * CSA2_IDX_BYTES, so, 0);
+        ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(r, voff_c + gi * 16 * CSA2_IDX_BYTES, so, 0);
+        ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(r, voff_s + gi * 16 * CSA2_IDX_BYTES, so, 0);
       }
     };
     bf16x8_t qa[MAXPAIRS][4];
@@ -250,7 +268,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     }
   } else {
     int64_t bl0, nb;
-    req_blocks(a.g, b, n, bl0, nb);
+    req_blocks(a.g, b, n, bl0, nb, PAGED);
     // 16 x bgroups summaries per wave.  A summary is 256 B (3.8x an entry's 68 B), so
     // with one entry chunk per wave the block tiles take one group per wave and finish
     // with the entry tiles; larger scans give them up to four.
@@ -263,7 +281,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     for (int gi = 0; gi < bgroups; ++gi) {
       const int64_t j = base + gi * 16 + m;
       const int64_t jl = j < nb ? j : nb - 1;
-      const uint16_t* sp = a.blk_sum + (bl0 + jl) * CSA2_IDX_D + 32 * g;
+      const int64_t row = PAGED ? page_of(a.g, b, jl) : bl0 + jl;
+      const uint16_t* sp = a.blk_sum + row * CSA2_IDX_D + 32 * g;
       bf16x8_t kb[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) kb[c] = as_bf16x8(load16(sp + 8 * c));
@@ -272,28 +291,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
   }
 }
 
-// Candidate-only scan: one wave per (kept block slot, row); scores the block's <= 64
-// entries for that row only.
+// Candidate-only scan: one wave per (kept block slot, row); scores the block's entries
+// that the row sees (<= 64), for that row only.
 __global__ __launch_bounds__(64) void k_scan_kept(ScanArgs a) {
   const int r = blockIdx.y;
   const int slot = blockIdx.x;
   int nk = a.n_kept[r];
   nk = nk < 0 ? 0 : (nk > a.kept_ld ? a.kept_ld : nk);
   if (slot >= nk) return;
+  const int64_t vis = row_len_raw(a.g, r);
   const int b = row_request(a.g, r);
   int64_t e0, n;
   req_entries(a.g, b, e0, n);
+  n = row_visible(a.g, vis, n);
   const int64_t blk = a.kept[(int64_t)r * a.kept_ld + slot];
   if (blk < 0 || blk * CSA2_BLOCK >= n) return;
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int64_t base = blk * CSA2_BLOCK;
+  const int64_t row0 = paged(a.g) ? page_of(a.g, b, blk) * CSA2_BLOCK : e0 + base;   // the block is one page
   u32x4_t kc[4];
   uint32_t ks[4];
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     int64_t e = base + gi * 16 + m;
     e = e < n ? e : n - 1;
-    const uint8_t* rec = a.idx_k + (e0 + e) * CSA2_IDX_BYTES;
+    const uint8_t* rec = a.idx_k + (row0 + (e - base)) * CSA2_IDX_BYTES;
     kc[gi] = load16_a4(rec + 16 * g);
     ks[gi] = rec[64 + g];
   }
@@ -312,16 +334,24 @@ __global__ __launch_bounds__(64) void k_scan_kept(ScanArgs a) {
 
 }  // namespace
 
+template <int PARTS, bool PAGED>
+static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
+  if (max_rows_per_req <= 2)
+    k_scan<1, PARTS, PAGED><<<grid, dim3(256), 0, st>>>(a);
+  else if (max_rows_per_req <= 4)
+    k_scan<2, PARTS, PAGED><<<grid, dim3(256), 0, st>>>(a);
+  else if (max_rows_per_req <= 8)
+    k_scan<4, PARTS, PAGED><<<grid, dim3(256), 0, st>>>(a);
+  else
+    k_scan<8, PARTS, PAGED><<<grid, dim3(256), 0, st>>>(a);
+}
+
 template <int PARTS>
 static void launch_scan_parts(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
-  if (max_rows_per_req <= 2)
-    k_scan<1, PARTS><<<grid, dim3(256), 0, st>>>(a);
-  else if (max_rows_per_req <= 4)
-    k_scan<2, PARTS><<<grid, dim3(256), 0, st>>>(a);
-  else if (max_rows_per_req <= 8)
-    k_scan<4, PARTS><<<grid, dim3(256), 0, st>>>(a);
+  if (a.g.page_table)
+    launch_scan_rows<PARTS, true>(a, max_rows_per_req, grid, st);
   else
-    k_scan<8, PARTS><<<grid, dim3(256), 0, st>>>(a);
+    launch_scan_rows<PARTS, false>(a, max_rows_per_req, grid, st);
 }
 
 #ifndef CSA2_SCAN_TARGET_WGS

@@ -41,6 +41,7 @@ static_assert(kLdsBlocks >= kMaxCand, "shared key buffer");
 struct SelShared {
   alignas(16) uint32_t hist[2][kBins];
   uint32_t red[2 * NW];
+  uint32_t cnt[NW];
   uint32_t wgt[NW], weq[NW];
   uint32_t mkey[kMemMax];
   uint32_t digit, above;
@@ -50,6 +51,7 @@ struct SelShared {
   int32_t flag;
   int32_t nk;
   int32_t kl[CSA2_KEEP_MAX + 2];
+  int32_t kpage[CSA2_KEEP_MAX + 2];   // pool page of each kept block (paged pools)
 };
 
 __device__ __forceinline__ void wave_chunks(int n, int& c0, int& c1) {
@@ -58,15 +60,24 @@ __device__ __forceinline__ void wave_chunks(int n, int& c0, int& c1) {
   c1 = (w + 1) * nch / NW;
 }
 
-// Key range of the valid items, reduced per wave into sh.red by the gather (one
-// barrier later every thread reads the workgroup range).
-__device__ __forceinline__ void range_publish(uint32_t lo, uint32_t hi, SelShared& sh) {
+// Key range and count of the valid (non-zero) items, reduced per wave into sh.red and
+// sh.cnt by the gather (one barrier later every thread reads the workgroup figures).
+__device__ __forceinline__ void range_publish(uint32_t lo, uint32_t hi, uint32_t cnt, SelShared& sh) {
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), kWave - 1);
   if ((threadIdx.x & (kWave - 1)) == 0) {
     sh.red[2 * (threadIdx.x / kWave)] = lo;
     sh.red[2 * (threadIdx.x / kWave) + 1] = hi;
+    sh.cnt[threadIdx.x / kWave] = cnt;
   }
+}
+
+// Valid items published by range_publish (after a barrier).
+__device__ __forceinline__ int valid_count(const SelShared& sh) {
+  int c = 0;
+  for (int w = 0; w < NW; ++w) c += (int)sh.cnt[w];
+  return c;
 }
 
 // k-th largest key among the valid items (1 <= k < valid count): T and n_gt = number of
@@ -273,7 +284,7 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // range and zeroes the first histogram buffer; the caller then needs one barrier.
 template <class ValidF, class LoadF>
 __device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShared& sh) {
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, cnt = 0u;
   for (int base = 0; base < n; base += NT * kGB) {
     float v[kGB];
     bool ok[kGB];
@@ -286,25 +297,28 @@ __device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShare
 #pragma unroll
     for (int u = 0; u < kGB; ++u) {
       const int i = base + u * NT + (int)threadIdx.x;
-      const uint32_t kk = ok[u] ? score_key(v[u]) : 0u;
+      const uint32_t kk = score_key(v[u]) & (0u - (uint32_t)ok[u]);   // masked, not branched
       if (i < n) kbuf[i] = kk;
-      if (kk) {
-        lo = min(lo, kk);
-        hi = max(hi, kk);
-      }
+      // Branch-free: an empty key (0) leaves the minimum, maximum and count alone.
+      lo = min(lo, kk ? kk : 0xFFFFFFFFu);
+      hi = max(hi, kk);
+      cnt += kk ? 1u : 0u;
     }
   }
   const int padded = (n + kWave - 1) / kWave * kWave;
   for (int i = n + (int)threadIdx.x; i < padded; i += NT) kbuf[i] = 0u;
-  range_publish(lo, hi, sh);
+  range_publish(lo, hi, cnt, sh);
   for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[0][i] = 0u;
 }
 
+template <bool PAGED>
 __device__ __forceinline__ int row_blocks(const SelectArgs& a, int r, int64_t& n) {
+  const int64_t vis = row_len_raw(a.g, r);
   const int b = row_request(a.g, r);
   int64_t e0, bl0, nb;
-  req_entries(a.g, b, e0, n);
-  req_blocks(a.g, b, n, bl0, nb);
+  req_entries(a.g, b, e0, n, PAGED);
+  n = row_visible(a.g, vis, n);
+  req_blocks(a.g, b, n, bl0, nb, PAGED);
   return (int)nb;
 }
 
@@ -323,22 +337,23 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
   if (nb <= kLdsBlocks) {
     gather(nb, [](int) { return true; }, [&](int i, bool ok) { return bs[ok ? i : 0]; }, kbuf, sh);
     __syncthreads();
-    cnt = sel_top([&](int i) { return kbuf[i]; }, nb, nb, a.n_keep, sh, emit);
+    cnt = sel_top([&](int i) { return kbuf[i]; }, nb, valid_count(sh), a.n_keep, sh, emit);
   } else {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0u;
     for (int i = threadIdx.x; i < nb; i += NT) {
       const uint32_t kk = score_key(bs[i]);
-      lo = min(lo, kk);
+      lo = min(lo, kk ? kk : 0xFFFFFFFFu);
       hi = max(hi, kk);
+      nv += kk ? 1u : 0u;
     }
-    range_publish(lo, hi, sh);
+    range_publish(lo, hi, nv, sh);
     for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[0][i] = 0u;
     __syncthreads();
     auto gkey = [&](int i) {
       const float v = bs[i < nb ? i : 0];
       return i < nb ? score_key(v) : 0u;
     };
-    cnt = sel_top(gkey, nb, nb, a.n_keep, sh, emit);
+    cnt = sel_top(gkey, nb, valid_count(sh), a.n_keep, sh, emit);
   }
   __syncthreads();
   // The newest block joins if the ranking left it out (it is the largest index, so the
@@ -358,7 +373,11 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
 }
 
 // Fine stage of row r over the kept blocks sh.kl[0 .. nk) (chunk s = kept block s,
-// lane = entry) or, with all_entries, over entries 0 .. n-1.
+// lane = entry) or, with all_entries, over entries 0 .. n-1.  Candidates are the items
+// with a key: positions the row sees whose score is not NaN.
+// PAGED: paged pools; the picks' pool rows then also go to a.sel_rows when it is set
+// (contiguous pools get an instantiation without that code).
+template <bool PAGED>
 __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_entries, SelShared& sh,
                      uint32_t* kbuf) {
   const float* sc = a.scores + (int64_t)r * a.ld;
@@ -367,12 +386,21 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_ent
   float* ss = a.sel_score ? a.sel_score + (int64_t)r * k : nullptr;
   auto pos_of = [&](int i) { return (int64_t)sh.kl[i / CSA2_BLOCK] * CSA2_BLOCK + (i % CSA2_BLOCK); };
   const int nk_c = nk > 0 ? nk : 1;   // slot index clamp for unconditional reads
-  int items, n_valid;
+  // Pool rows of the picks (attention over paged pools): the page of each kept block
+  // is looked up once here, so the emit below translates from LDS.
+  int32_t* rows = (PAGED && a.sel_rows && !all_entries) ? a.sel_rows + (int64_t)r * k : nullptr;
+  if (PAGED && rows) {
+    const int b = row_request(a.g, r);
+    for (int s = threadIdx.x; s < nk; s += NT) {
+      const int64_t kb = sh.kl[s];
+      const bool ok = kb >= 0 && kb * CSA2_BLOCK < n;
+      sh.kpage[s] = ok ? (int32_t)(page_of(a.g, b, kb) * CSA2_BLOCK) : 0;
+    }
+  }
+  int items;
   if (all_entries) {
     items = (int)(n < kMaxCand ? n : kMaxCand);
-    n_valid = items;
     gather(items, [](int) { return true; }, [&](int i, bool ok) { return sc[ok ? i : 0]; }, kbuf, sh);
-    __syncthreads();
   } else {
     items = nk * CSA2_BLOCK;
     auto slot_pos = [&](int i) {
@@ -384,43 +412,37 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_ent
       return p >= 0 && p < n;
     };
     gather(items, valid, [&](int i, bool ok) { return sc[ok ? slot_pos(i) : 0]; }, kbuf, sh);
-    // Valid candidates: thread s counts kept block s's entries; per-wave sums.
-    uint32_t cv = 0u;
-    if ((int)threadIdx.x < nk) {
-      const int64_t kb = sh.kl[threadIdx.x];
-      if (kb >= 0 && kb * CSA2_BLOCK < n) cv = (uint32_t)min<int64_t>(CSA2_BLOCK, n - kb * CSA2_BLOCK);
-    }
-    const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cv), kWave - 1);
-    if ((threadIdx.x & (kWave - 1)) == 0) sh.wgt[threadIdx.x / kWave] = wsum;
-    __syncthreads();
-    n_valid = 0;
-    for (int w = 0; w < NW; ++w) n_valid += (int)sh.wgt[w];
   }
-  const int take = sel_top([&](int i) { return kbuf[i]; }, items, n_valid, k, sh, [&](int pos, int i) {
+  __syncthreads();
+  const int take = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), k, sh, [&](int pos, int i) {
     sel[pos] = all_entries ? i : (int32_t)pos_of(i);
     if (ss) ss[pos] = key_score(kbuf[i]);
+    if (PAGED && rows) rows[pos] = sh.kpage[i / CSA2_BLOCK] + (i % CSA2_BLOCK);
   });
   for (int i = take + threadIdx.x; i < k; i += NT) {
     sel[i] = -1;
     if (ss) ss[i] = 0.f;
+    if (PAGED && rows) rows[i] = -1;
   }
   if (threadIdx.x == 0) a.n_sel[r] = take;
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(NT) void k_block_select(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
   int64_t n;
-  const int nb = row_blocks(a, blockIdx.x, n);
+  const int nb = row_blocks<PAGED>(a, blockIdx.x, n);
   coarse(a, blockIdx.x, nb, sh, kbuf);
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(NT) void k_topk(SelectArgs a, int all_entries) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kMaxCand];
   const int r = blockIdx.x;
   int64_t n;
-  row_blocks(a, r, n);
+  row_blocks<PAGED>(a, r, n);
   int nk = 0;
   if (!all_entries) {
     nk = a.n_kept[r];
@@ -429,38 +451,48 @@ __global__ __launch_bounds__(NT) void k_topk(SelectArgs a, int all_entries) {
     for (int i = threadIdx.x; i < nk; i += NT) sh.kl[i] = a.kept[(int64_t)r * a.kept_ld + i];
     __syncthreads();
   }
-  fine(a, r, n, nk, all_entries != 0, sh, kbuf);
+  fine<PAGED>(a, r, n, nk, all_entries != 0, sh, kbuf);
 }
 
 // Both stages for one row; the block keys and the candidate keys share one LDS buffer.
+template <bool PAGED>
 __global__ __launch_bounds__(NT) void k_select_fused(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
   const int r = blockIdx.x;
   int64_t n;
-  const int nb = row_blocks(a, r, n);
+  const int nb = row_blocks<PAGED>(a, r, n);
   coarse(a, r, nb, sh, kbuf);
   __syncthreads();
-  fine(a, r, n, sh.nk, false, sh, kbuf);
+  fine<PAGED>(a, r, n, sh.nk, false, sh, kbuf);
 }
 
 }  // namespace
 
 hipError_t launch_block_select(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  k_block_select<<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+  if (a.g.page_table)
+    k_block_select<true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+  else
+    k_block_select<false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  k_topk<<<dim3(a.g.R), dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
+  if (a.g.page_table)
+    k_topk<true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
+  else
+    k_topk<false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_select_fused(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  k_select_fused<<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+  if (a.g.page_table)
+    k_select_fused<true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+  else
+    k_select_fused<false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -5,4 +5,6 @@ from .generator import (  # noqa: F401
     Workload,
     make_config,
     make_workload,
+    to_paged,
+    verify_row_len,
 )

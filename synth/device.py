@@ -38,11 +38,16 @@ def upload(wl, device="cuda") -> DeviceWorkload:
     from sparse_decode_attention_csa2_amd import Ragged
     dev = torch.device(device)
     rows_per = np.diff(wl.row_off)
-    rg = Ragged(entry_off=_t(wl.entry_off, dev), block_off=_t(wl.block_off, dev), row_off=_t(wl.row_off, dev),
-                row_req=_t(wl.row_req, dev), row_swa_start=_t(wl.row_swa_start, dev),
-                row_swa_len=_t(wl.row_swa_len, dev), max_entries=wl.max_entries, total_entries=wl.total_entries,
-                total_blocks=int(wl.block_off[-1]), swa_tokens=int(wl.swa_off[-1]),
-                max_rows_per_request=int(rows_per.max()) if rows_per.size else 1)
+    paged = getattr(wl, "page_table", None) is not None
+    row_len = getattr(wl, "row_len", None)
+    rg = Ragged(entry_off=_t(wl.entry_off, dev), block_off=None if paged else _t(wl.block_off, dev),
+                row_off=_t(wl.row_off, dev), row_req=_t(wl.row_req, dev), row_swa_start=_t(wl.row_swa_start, dev),
+                row_swa_len=_t(wl.row_swa_len, dev), max_entries=wl.max_entries,
+                total_entries=int(wl.idx_k.shape[0]), total_blocks=int(wl.blk_sum.shape[0]),
+                swa_tokens=int(wl.swa_off[-1]), max_rows_per_request=int(rows_per.max()) if rows_per.size else 1,
+                row_len=None if row_len is None else _t(np.asarray(row_len, dtype=np.int64), dev),
+                page_table=_t(wl.page_table, dev) if paged else None,
+                total_pages=int(wl.total_pages) if paged else 0)
     return DeviceWorkload(rg=rg, idx_k=_t(wl.idx_k, dev), main_kv=_t(wl.main_kv, dev), blk_sum=_t(wl.blk_sum, dev),
                           swa=_t(wl.swa, dev), swa_scale=_t(wl.swa_scale, dev), q=_t(wl.q, dev),
                           q_idx=_t(wl.q_idx, dev), w=_t(wl.w, dev))

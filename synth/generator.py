@@ -30,8 +30,10 @@ request ``b`` of a config does not depend on how many requests follow it:
 * ``(seed, 1, b, 3, c)``        indexer keys [<=16384, 128] N(0,1) of chunk c;
 * ``(seed, 1, b, 4, c)``        main latents [<=16384, 512] N(0,1) of chunk c;
 * ``(seed, 1, b, 5)``           window tokens [T_b, 512] N(0,1).
+* ``(seed, 2, 1)``              paged copies: the page permutation, then the bytes of
+                                spare pages and of the unused tail rows of last pages.
 
-All draws are float32.
+All draws are float32 (page bytes: uniform uint8 / uint16).
 """
 from __future__ import annotations
 
@@ -173,6 +175,9 @@ class Workload:
     q_idx: np.ndarray         # uint16 (bf16 bits) [R, 8, 128]
     w: np.ndarray             # float32 [R, 8]
     needles: list = field(default_factory=list)  # per request: int64 positions
+    page_table: np.ndarray | None = None   # int32 [B][pages_ld]: paged pools (then the pools are pages)
+    total_pages: int = 0
+    row_len: np.ndarray | None = None      # int64 [R]: entries each row sees (None: all)
     k: int = TOP_K
     n_keep: int = N_KEEP
     keep_newest: int = 1
@@ -316,6 +321,63 @@ def make_workload(name: str, seed: int, n_entries: list, rows_per_req: list | in
                     row_req=row_req, row_swa_start=row_swa_start, row_swa_len=row_swa_len,
                     idx_k=idx_k, main_kv=main_kv, blk_sum=blk_sum, swa=swa, swa_scale=swa_scale,
                     q=q, q_idx=q_idx, w=w, needles=needles)
+
+
+def to_paged(wl: Workload, seed: int | None = None, spare_pages: int | None = None) -> Workload:
+    """The same logical workload over paged pools.
+
+    The idx_k / main_kv pools are cut into 64-entry pages and the summary pool into one
+    summary per page; request b's page j (entries 64j .. 64j+63, summary j) goes to a
+    physical page drawn by a seeded permutation of all pages, so a request's pages are
+    scattered and interleaved with other requests'.  ``spare_pages`` extra pages (default
+    about 1/8 of the total) and the unused tail rows of each request's last page hold
+    random bytes, so any read outside the page table's entries changes the results.
+    Page-table slots past a request's last page are -1.
+    """
+    seed = wl.seed if seed is None else seed
+    B = wl.num_requests
+    nbs = [-(-wl.n_entries(b) // SUMMARY_BLOCK) for b in range(B)]
+    used = int(sum(nbs))
+    spare = max(1, used // 8) if spare_pages is None else int(spare_pages)
+    P = used + spare
+    rng = _rng(seed, 2, 1)
+    perm = rng.permutation(P).astype(np.int32)
+    pages_ld = max([1] + nbs)
+    page_table = np.full((B, pages_ld), -1, dtype=np.int32)
+    idx_k = rng.integers(0, 256, size=(P * SUMMARY_BLOCK, IDX_BYTES), dtype=np.uint8)
+    main_kv = rng.integers(0, 256, size=(P * SUMMARY_BLOCK, MAIN_BYTES), dtype=np.uint8)
+    blk_sum = rng.integers(0, 1 << 16, size=(P, D_IDX), dtype=np.uint16)
+    i = 0
+    for b in range(B):
+        e0, n = int(wl.entry_off[b]), wl.n_entries(b)
+        for j in range(nbs[b]):
+            p = int(perm[i])
+            i += 1
+            page_table[b, j] = p
+            lo, hi = 64 * j, min(n, 64 * j + 64)
+            idx_k[64 * p:64 * p + hi - lo] = wl.idx_k[e0 + lo:e0 + hi]
+            main_kv[64 * p:64 * p + hi - lo] = wl.main_kv[e0 + lo:e0 + hi]
+            blk_sum[p] = wl.blk_sum[int(wl.block_off[b]) + j]
+    out = Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+    out.name = wl.name + "_paged"
+    out.idx_k, out.main_kv, out.blk_sum = idx_k, main_kv, blk_sum
+    out.page_table, out.total_pages = page_table, P
+    return out
+
+
+def verify_row_len(wl: Workload) -> np.ndarray:
+    """Entries each row sees when the rows of a request are consecutive verify positions.
+
+    Row j of a request with m rows sits m-1-j tokens before the request's last row; with
+    two tokens pooled per global entry and the last row completing a pair, it sees
+    N_b - ceil((m-1-j)/2) entries (at least 0)."""
+    rl = np.zeros(wl.num_rows, dtype=np.int64)
+    for b in range(wl.num_requests):
+        r0, r1 = int(wl.row_off[b]), int(wl.row_off[b + 1])
+        m = r1 - r0
+        for j in range(m):
+            rl[r0 + j] = max(0, wl.n_entries(b) - (m - j) // 2)
+    return rl
 
 
 # ---------------------------------------------------------------------------------

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa2_version() == 1
+    assert lib.csa2_version() == 2
     for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported parameter"),
                        (3, b"workspace too small"), (4, b"HIP error")):
         assert lib.csa2_status_string(code) == text
@@ -48,6 +48,9 @@ def _rg(**kw):
     r.max_entries, r.total_entries = kw.get("max_entries", 100), kw.get("total_entries", 100)
     r.total_blocks, r.swa_tokens = kw.get("total_blocks", 2), kw.get("swa_tokens", 128)
     r.max_rows_per_request = kw.get("mrpr", 1)
+    r.row_len = kw.get("row_len", None)
+    r.page_table = kw.get("page_table", None)
+    r.pages_ld, r.total_pages = kw.get("pages_ld", 0), kw.get("total_pages", 0)
     return r
 
 
@@ -133,3 +136,31 @@ def test_stream_read_validates_before_launch(lib):
     assert lib.csa2_debug_stream_read(None, -16, None, None) == csa2.ERR_INVALID_ARG
     assert lib.csa2_debug_stream_read(None, 16, None, None) == csa2.ERR_INVALID_ARG      # null source
     assert lib.csa2_debug_stream_read(0x10008, 16, 0x20000, None) == csa2.ERR_INVALID_ARG  # misaligned
+
+
+def test_paged_descriptor_checks(lib):
+    fake = 0x10000
+    args = (16, 16, 16, None, None, 0, 16, 100, None)
+    # 100 entries need 2 pages per request; the pools hold 2 pages (128 rows, 2 summaries).
+    ok = dict(page_table=fake, pages_ld=2, total_pages=2, total_entries=128, total_blocks=2)
+    rg = _rg(**{**ok, "pages_ld": 1})
+    assert lib.csa2_index_score(ctypes.byref(rg), *args) == csa2.ERR_INVALID_ARG
+    assert b"pages_ld" in lib.csa2_last_error()
+    rg = _rg(**{**ok, "total_pages": 0})
+    assert lib.csa2_index_score(ctypes.byref(rg), *args) == csa2.ERR_INVALID_ARG
+    rg = _rg(**{**ok, "total_pages": 3})                    # more pages than the pools hold
+    assert lib.csa2_index_score(ctypes.byref(rg), *args) == csa2.ERR_INVALID_ARG
+    rg = _rg(**{**ok, "total_entries": 127})
+    assert lib.csa2_index_score(ctypes.byref(rg), *args) == csa2.ERR_INVALID_ARG
+    # block_off may be NULL with a page table, not without one.
+    rg = _rg(block_off=None)
+    assert lib.csa2_index_score(ctypes.byref(rg), *args) == csa2.ERR_INVALID_ARG
+    assert b"block_off" in lib.csa2_last_error()
+    # The paged standalone attention also needs room for the translated rows.
+    rg = _rg(R=1, **ok)
+    plain = _rg(R=1)
+    need = lib.csa2_sparse_attn_workspace_size(ctypes.byref(rg), 512)
+    assert need >= lib.csa2_sparse_attn_workspace_size(ctypes.byref(plain), 512) + 512 * 4
+    st = lib.csa2_sparse_attn(ctypes.byref(rg), 16, 16, 16, 16, 512, 16, 16, ctypes.c_float(0.044), 16, 16, 256,
+                              need - 1, None)
+    assert st == csa2.ERR_WORKSPACE_TOO_SMALL

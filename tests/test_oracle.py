@@ -262,3 +262,132 @@ def test_config0_oracle_runs(i):
     rr = oracle.decode(wl)[0]
     assert rr["sel"].size == 512 and rr["kept"].size == 32
     assert np.all(np.isfinite(rr["out"]))
+
+
+# ---------------------------------------------------------------------------------
+# Row visibility, score check and paged pools.
+# ---------------------------------------------------------------------------------
+
+def _truncated(wl, r, v):
+    """Row r alone, over its request cut to its first v entries (arrays sliced here,
+    independently of the oracle's row-visibility code)."""
+    from synth import Workload
+    b = int(wl.row_req[r])
+    e0, b0 = int(wl.entry_off[b]), int(wl.block_off[b])
+    nb = -(-v // 64)
+    s0, sl = int(wl.row_swa_start[r]), int(wl.row_swa_len[r])
+    return Workload(name="cut", seed=0, n_tokens=[v], entry_off=np.array([0, v], dtype=np.int64),
+                    block_off=np.array([0, nb], dtype=np.int64), row_off=np.array([0, 1], dtype=np.int32),
+                    swa_off=np.array([0, sl], dtype=np.int64), row_req=np.zeros(1, dtype=np.int32),
+                    row_swa_start=np.zeros(1, dtype=np.int64), row_swa_len=np.array([sl], dtype=np.int32),
+                    idx_k=wl.idx_k[e0:e0 + v], main_kv=wl.main_kv[e0:e0 + v], blk_sum=wl.blk_sum[b0:b0 + nb],
+                    swa=wl.swa[s0:s0 + sl], swa_scale=wl.swa_scale[s0:s0 + sl], q=wl.q[r:r + 1],
+                    q_idx=wl.q_idx[r:r + 1], w=wl.w[r:r + 1])
+
+
+def test_row_len_equals_truncated_request():
+    # A row that sees V entries decodes exactly like a request holding only those V.
+    wl = make_workload("rl", 31, [64 * 90 + 17, 700], rows_per_req=[4, 2], n_needles=8)
+    wl.row_len = np.array([64 * 90 + 17, 64 * 90, 64 * 70 + 1, 5000, 700, 1], dtype=np.int64)
+    got = oracle.decode(wl, k=300, n_keep=40)
+    for r in range(wl.num_rows):
+        v = int(wl.row_len[r])
+        ref = oracle.decode(_truncated(wl, r, v), k=300, n_keep=40)[0]
+        assert got[r]["block_scores"].shape[0] == -(-v // 64)
+        for key in ("kept", "sel", "out", "lse", "block_scores"):
+            assert np.array_equal(got[r][key], ref[key]), (r, key)
+        assert got[r]["sel"].size == 0 or got[r]["sel"].max() < v
+
+
+def test_row_len_zero_and_beyond():
+    wl = make_workload("rl0", 32, [300], rows_per_req=[3], n_needles=2)
+    wl.row_len = np.array([0, 10 ** 9, -4], dtype=np.int64)   # clamps to 0 .. N
+    got = oracle.decode(wl)
+    assert got[0]["sel"].size == 0 and got[0]["kept"].size == 0 and got[2]["sel"].size == 0
+    full = oracle.decode(make_workload("rl0", 32, [300], rows_per_req=[3], n_needles=2))
+    assert np.array_equal(got[1]["sel"], full[1]["sel"]) and np.array_equal(got[1]["out"], full[1]["out"])
+    # No main entries: attention over the window alone.
+    ro, rl = oracle.joint_attention(oracle.bf16_value(wl.q[0]), oracle.row_keys(wl, 0, np.zeros(0)), wl.sm_scale)
+    assert np.array_equal(got[0]["out"], ro) and np.array_equal(got[0]["lse"], rl)
+
+
+def _is_topk(positions, scores, k, sel):
+    """True iff ``sel`` is the unique set of min(k, #non-NaN) non-NaN candidates such that
+    every pick beats every non-pick by (score desc, position asc)."""
+    valid = {int(t): float(s) for t, s in zip(positions, scores) if not math.isnan(s)}
+    sel = [int(t) for t in sel]
+    if len(set(sel)) != len(sel) or any(t not in valid for t in sel) or len(sel) != min(k, len(valid)):
+        return False
+    rest = set(valid) - set(sel)
+    return all(valid[s] > valid[u] or (valid[s] == valid[u] and s < u) for s in sel for u in rest)
+
+
+def test_topk_skips_nan_scores():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        n = int(rng.integers(1, 60))
+        pos = np.sort(rng.choice(1000, size=n, replace=False))
+        sc = rng.integers(-3, 4, size=n).astype(np.float64)
+        sc[rng.random(n) < 0.3] = np.nan
+        for k in (1, 3, n // 2 + 1, n, n + 5):
+            sel = oracle.top_k(pos, sc, k)
+            assert np.all(np.diff(sel) > 0)
+            assert _is_topk(pos, sc, k, sel), (trial, k)
+    assert oracle.top_k(np.arange(4), np.full(4, np.nan), 2).size == 0
+
+
+def test_keep_blocks_skips_nan_scores():
+    rng = np.random.default_rng(6)
+    for trial in range(40):
+        nb = int(rng.integers(1, 40))
+        bs = rng.integers(0, 5, size=nb).astype(np.float64)
+        bs[rng.random(nb) < 0.3] = np.nan
+        for n_keep in (1, 4, nb):
+            for newest in (True, False):
+                kept = oracle.keep_blocks(bs, n_keep, newest).tolist()
+                # Either the kept set is the ranked top set itself, or (newest rule) the
+                # top set plus the newest block that the ranking left out.
+                ok = _is_topk(np.arange(nb), bs, n_keep, kept)
+                if not ok and newest and kept and kept[-1] == nb - 1:
+                    ok = _is_topk(np.arange(nb), bs, n_keep, kept[:-1])
+                assert ok, (trial, n_keep, newest)
+                assert (nb - 1 in kept) or not newest
+                assert np.all(np.diff(kept) > 0)
+
+
+def test_decode_never_selects_nan_scored_entries():
+    # Entries with an E8M0 NaN scale byte score NaN; the needles (which would rank first)
+    # are given one, so the selection must fall back to the other entries.
+    wl = make_workload("nan", 33, [64 * 80 + 9], rows_per_req=[2], n_needles=16)
+    bad = wl.needles[0]
+    wl.idx_k[bad, 64] = 255
+    got = oracle.decode(wl, k=200, n_keep=20)
+    for r in range(2):
+        s = got[r]["scores"]
+        assert np.all(np.isnan(s[bad]))
+        assert not set(bad.tolist()) & set(got[r]["sel"].tolist())
+        assert _is_topk(got[r]["cand"], got[r]["cand_scores"], 200, got[r]["sel"])
+    # A block summary scoring NaN is never ranked, but the newest-block rule still keeps
+    # the newest block.
+    wl.blk_sum[[3, 80]] = 0x7FC0
+    got = oracle.decode(wl, k=200, n_keep=20)
+    for r in range(2):
+        assert 3 not in got[r]["kept"] and 80 in got[r]["kept"]
+
+
+def test_paged_pools_match_contiguous():
+    # Pages scattered over a pool with spare pages of random bytes: reading any row the
+    # page table does not name changes the result.
+    from synth import to_paged
+    wl = make_workload("pg", 34, [64 * 40 + 5, 1000, 64, 1, 0], rows_per_req=[1, 3, 2, 1, 1], n_needles=6)
+    pw = to_paged(wl)
+    assert pw.page_table.shape == (5, 41) and pw.total_pages > 41 + 16 + 1 + 1
+    assert len(set(pw.page_table[pw.page_table >= 0].tolist())) == int((pw.page_table >= 0).sum())
+    a, b = oracle.decode(wl, k=300, n_keep=16), oracle.decode(pw, k=300, n_keep=16)
+    for r, (x, y) in enumerate(zip(a, b)):
+        for key in ("kept", "sel", "out", "lse", "block_scores", "scores"):
+            assert np.array_equal(x[key], y[key]), (r, key)
+    # The page table is what locates the data: a swapped pair of pages changes the keys.
+    pw.page_table[1, [0, 1]] = pw.page_table[1, [1, 0]]
+    c = oracle.decode(pw, rows=[1], k=300, n_keep=16)[0]
+    assert not np.array_equal(c["scores"], a[1]["scores"])
