@@ -453,13 +453,25 @@ def main() -> int:
         res["attention_roofline"] = aroof
         torch.cuda.empty_cache()
     if not args.no_configs:
+        from synth import to_paged, verify_row_len
         per = {}
-        for i in (0, 2, 3, 4, 5):
-            if i == args.config:
-                continue
+
+        def paged_rowlen(i):
             w = make_config(i)
+            w.row_len = verify_row_len(w)
+            w = to_paged(w)
+            w.name = w.name.replace("_paged", "_paged_rowlen")
+            return w
+
+        # The other decode workloads, then two served shapes: the headline over paged
+        # pools, and the verify batch over paged pools with per-row visible lengths.
+        cases = [(i, lambda i=i: make_config(i)) for i in (0, 2, 3, 4, 5) if i != args.config]
+        cases += [("paged", lambda: to_paged(make_config(args.config))), ("paged_rowlen", lambda: paged_rowlen(3))]
+        for _, mk in cases:
+            w = mk()
             mi = measure_decode(csa2, hip, w, steps=max(64, min(K, 400)), warmup=8)
             per[w.name] = {"requests": w.num_requests, "rows": w.num_rows, "entries": w.total_entries,
+                           "paged": w.page_table is not None, "row_len": w.row_len is not None,
                            "rows_per_s": mi["rows_per_s"], "ms_per_step": mi["ms_per_step"],
                            "step_latency_us": mi["step_latency_us"],
                            "stages_us_eager": mi["stages_us_eager"], "input_replicas": mi["input_replicas"]}

@@ -126,17 +126,18 @@ typedef struct csa2_ragged {
  *   scores[r*ld + t] = sum_{h<8} w_idx[r*8+h] * max(0, q_h . k_t),
  * q_h = q_idx[(r*8+h)*128 .. +127] (bf16 bit patterns), k_t the dequantised 68-B key.
  * idx_k: [total_entries][68] bytes.  ld >= max_entries.
- * kept_blocks == NULL: every entry is scored.  Otherwise only the entries of the blocks
- * kept_blocks[r*kept_ld + j], j < n_kept[r], are scored (candidate-only scan); other
- * positions of scores are left untouched.  The rows of one request share one read of
- * its keys.
+ * kept_blocks == NULL: every entry of the request is scored, also past a row's visible
+ * length (the rows of one request share one read of its keys).  Otherwise only the
+ * entries the row sees of the blocks kept_blocks[r*kept_ld + j], j < n_kept[r], are
+ * scored (candidate-only scan); other positions of scores are left untouched.
  */
 int csa2_index_score(const csa2_ragged* rg, const uint8_t* idx_k, const uint16_t* q_idx, const float* w_idx,
                      const int32_t* kept_blocks, const int32_t* n_kept, int32_t kept_ld,
                      float* scores, int64_t ld, void* stream);
 
 /*
- * Step (2a): coarse block filter.  Block j of the row's request (nb = ceil(N/64) blocks)
+ * Step (2a): coarse block filter.  Block j of the row's request (nb = ceil(V/64) blocks,
+ * V = the entries the row sees)
  * scores s_j = sum_h w_h * max(0, q_h . summary_j) into blk_scores[r*blk_ld + j]
  * (blk_ld >= ceil(max_entries/64)).  If nb <= n_keep every block is kept; otherwise the
  * n_keep best blocks (ties to the lower j) plus, if keep_newest, block nb-1.  The kept
@@ -149,8 +150,9 @@ int csa2_block_filter(const csa2_ragged* rg, const uint16_t* blk_sum, const uint
                       int32_t* kept_blocks, int32_t* n_kept, float* blk_scores, int64_t blk_ld, void* stream);
 
 /*
- * Step (2b): fine top-k.  Candidates are the entries of the row's kept blocks (the
- * newest block may be partial); the k best scores (ties to the lower position) are
+ * Step (2b): fine top-k.  Candidates are the entries the row sees of its kept blocks
+ * (the newest block may be partial), NaN scores excepted; the k best scores (ties to
+ * the lower position) are
  * written in ascending position to sel_idx[r*k + i], their count min(k, candidates) to
  * n_sel[r], unused slots -1; sel_score (nullable) receives the matching scores.
  * kept_blocks == NULL: every entry of the request is a candidate (max_entries <=
@@ -162,14 +164,17 @@ int csa2_topk(const csa2_ragged* rg, const float* scores, int64_t ld,
 
 /*
  * Step (3): joint-softmax latent attention.  Row r's keys are the main entries
- * sel_idx[r*sel_ld + i], i < n_sel[r] (request-local positions; negative ones are
- * skipped), followed by the window tokens row_swa_start[r] .. +row_swa_len[r]-1.
+ * sel_idx[r*sel_ld + i], i < n_sel[r] (request-local positions; negative ones and those
+ * the row does not see are skipped), followed by the window tokens
+ * row_swa_start[r] .. +row_swa_len[r]-1.
  * K = V = the 512-dim dequantised latent.  For each head h:
  *   z_i = sm_scale * q_h . x_i,  out[(r*64+h)*512 + d] = sum_i softmax(z)_i x_i[d],
  *   lse[r*64+h] = log sum_i exp(z_i)   (natural log; -inf and out = 0 with no keys).
  * q: [R][64][512] bf16; main_kv: [total_entries][288]; swa: [swa_tokens][512] E4M3FN;
  * swa_scale: [swa_tokens] fp32; out fp32 [R][64][512]; lse fp32 [R][64].
- * ws: device workspace of at least csa2_sparse_attn_workspace_size(rg, sel_ld) bytes.
+ * ws: device workspace of at least csa2_sparse_attn_workspace_size(rg, sel_ld) bytes
+ * (with paged pools it also holds the positions translated to pool rows, which a first
+ * kernel writes).
  */
 int csa2_sparse_attn(const csa2_ragged* rg, const uint16_t* q, const uint8_t* main_kv,
                      const int32_t* sel_idx, const int32_t* n_sel, int32_t sel_ld,
@@ -177,7 +182,9 @@ int csa2_sparse_attn(const csa2_ragged* rg, const uint16_t* q, const uint8_t* ma
                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_workspace_size(const csa2_ragged* rg, int32_t sel_ld);
 
-/* The whole path on one stream: (2a) and (1), then (2b), then (3). */
+/* The whole path on one stream: (2a) and (1), then (2b), then (3).  With paged pools the
+ * fine top-k also writes the picks' pool rows into the workspace (address translation
+ * fused into the selection) and attention reads those. */
 typedef struct csa2_decode_args {
   csa2_ragged rg;
   const uint8_t* idx_k;        /* [total_entries][68] */
