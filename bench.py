@@ -189,7 +189,7 @@ def graph_kernel_ms(hip, fns, replays: int) -> float:
     return elapsed_ms(hip, ev[0], ev[1]) / n
 
 
-def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128):
+def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128, qp_route: int = 0):
     """Graph-replayed decode steps over rotating input copies; returns timings."""
     import torch
     from synth.device import upload
@@ -197,7 +197,7 @@ def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128):
     n_rep = min(max_reps, max(2, math.ceil(2 * MALL_BYTES / max(1, touched_bytes(wl))) + 1))
     reps = replicate(dw, n_rep)
     decs = [csa2.Decoder(*r.decode_inputs(), k=wl.k, n_keep=wl.n_keep, sm_scale=wl.sm_scale,
-                         keep_intermediates=False) for r in reps]
+                         keep_intermediates=False, qp_route=qp_route) for r in reps]
     for d in decs:
         d.run()
     torch.cuda.synchronize()
@@ -465,13 +465,17 @@ def main() -> int:
 
         # The other decode workloads, then two served shapes: the headline over paged
         # pools, and the verify batch over paged pools with per-row visible lengths.
-        cases = [(i, lambda i=i: make_config(i)) for i in (0, 2, 3, 4, 5) if i != args.config]
-        cases += [("paged", lambda: to_paged(make_config(args.config))), ("paged_rowlen", lambda: paged_rowlen(3))]
-        for _, mk in cases:
+        # The MXFP8 Q/P route of the attention on the headline and 64-row workloads.
+        cases = [(0, lambda i=i: make_config(i)) for i in (0, 2, 3, 4, 5) if i != args.config]
+        cases += [(0, lambda: to_paged(make_config(args.config))), (0, lambda: paged_rowlen(3))]
+        cases += [(csa2.QP_MXFP8, lambda: make_config(args.config)), (csa2.QP_MXFP8, lambda: make_config(5))]
+        for route, mk in cases:
             w = mk()
-            mi = measure_decode(csa2, hip, w, steps=max(64, min(K, 400)), warmup=8)
-            per[w.name] = {"requests": w.num_requests, "rows": w.num_rows, "entries": w.total_entries,
+            mi = measure_decode(csa2, hip, w, steps=max(64, min(K, 400)), warmup=8, qp_route=route)
+            name = w.name + ("_mxfp8" if route == csa2.QP_MXFP8 else "")
+            per[name] = {"requests": w.num_requests, "rows": w.num_rows, "entries": w.total_entries,
                            "paged": w.page_table is not None, "row_len": w.row_len is not None,
+                           "qp_route": "mxfp8" if route == csa2.QP_MXFP8 else "bf16",
                            "rows_per_s": mi["rows_per_s"], "ms_per_step": mi["ms_per_step"],
                            "step_latency_us": mi["step_latency_us"],
                            "stages_us_eager": mi["stages_us_eager"], "input_replicas": mi["input_replicas"]}

@@ -182,6 +182,20 @@ int csa2_sparse_attn(const csa2_ragged* rg, const uint16_t* q, const uint8_t* ma
                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_workspace_size(const csa2_ragged* rg, int32_t sel_ld);
 
+/* Arithmetic routes of step (3) (ktransformers issue mirror "Support for Deepseek V4.1
+ * Flash": sparse MLA runs either in full BF16 or with Q and P rounded to MXFP8).
+ *   CSA2_QP_BF16 : Q as given (bf16), P to about 2^-17 relative (fp32 accuracy).
+ *   CSA2_QP_MXFP8: Q (per head, blocks of 32 latent dims) and P (per head, blocks of 32
+ *                  consecutive keys in key order, the weight on each key's stored codes,
+ *                  i.e. p times the window scale for window tokens) are rounded to MXFP8
+ *                  (OCP MX: E4M3 elements, shared exponent floor(log2(block amax)) - 8,
+ *                  round to nearest even, saturating at 448) before their products;
+ *                  the softmax normaliser and lse use the unrounded p.  P is computed
+ *                  against the running maximum of the key range a workgroup covers, so
+ *                  its rounding depends on the split plan. */
+#define CSA2_QP_BF16  0
+#define CSA2_QP_MXFP8 1
+
 /* The whole path on one stream: (2a) and (1), then (2b), then (3).  With paged pools the
  * fine top-k also writes the picks' pool rows into the workspace (address translation
  * fused into the selection) and attention reads those. */
@@ -211,6 +225,7 @@ typedef struct csa2_decode_args {
   void* const* events;         /* nullable: CSA2_DECODE_EVENTS hipEvent_t handles, recorded on `stream`
                                   before the first kernel and after each stage (scan, select,
                                   attention, merge) for per-stage timing; recording adds no sync */
+  int32_t qp_route;            /* CSA2_QP_BF16 (default) or CSA2_QP_MXFP8 */
 } csa2_decode_args;
 
 #define CSA2_DECODE_EVENTS 5
@@ -227,6 +242,10 @@ size_t csa2_decode_workspace_size(const csa2_decode_args* a);
 #define CSA2_DQ_SWA  2
 int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales, int64_t n, float* out,
                        void* stream);
+
+/* Test hook: the attention kernel's MXFP8 rounding (CSA2_QP_MXFP8) over x[0 .. n-1] in
+ * blocks of 32 consecutive values (n a multiple of 32), results as exact fp32 in out. */
+int csa2_debug_mxfp8(const float* x, int64_t n, float* out, void* stream);
 
 /* Measurement hook, for callers that want the bandwidth a plain streaming read reaches
  * on this device (the reference the indexer scan is compared with): reads `bytes` bytes

@@ -225,6 +225,103 @@ def joint_attention(q: np.ndarray, keys: np.ndarray, sm_scale: float) -> tuple[n
 
 
 # ---------------------------------------------------------------------------------
+# O7b. The MXFP8 Q/P route of the attention ([KT]: sparse MLA with Q and P rounded to
+# MXFP8 instead of full BF16).
+# ---------------------------------------------------------------------------------
+
+E4M3_GRID = E4M3[:127]          # codes 0 .. 126: the non-negative finite values, ascending
+
+
+def mxfp8_round(x: np.ndarray, block: int = 32) -> np.ndarray:
+    """OCP MX rounding of the last axis in blocks of ``block`` values (MXFP8: E4M3
+    elements, one E8M0 scale per block): shared exponent s = floor(log2(block amax)) - 8
+    (8 = E4M3's largest exponent), clamped to -127 .. 127; each value becomes the E4M3
+    value nearest to x / 2^s (ties to the even code, magnitudes above 448 to 448) times
+    2^s.  The last axis is zero-padded to whole blocks for the scale and cut back."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    nb = -(-n // block)
+    xp = np.zeros(x.shape[:-1] + (nb * block,))
+    xp[..., :n] = x
+    xb = xp.reshape(x.shape[:-1] + (nb, block))
+    amax = np.abs(xb).max(axis=-1, keepdims=True)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))          # amax = f * 2^e, f in [0.5, 1)
+    s = np.clip(e - 1 - 8, -127, 127)
+    s = np.where(amax > 0, s, -127)
+    y = np.minimum(np.abs(xb) / np.ldexp(1.0, s), 448.0)
+    hi = np.clip(np.searchsorted(E4M3_GRID, y), 1, 126)   # first grid value >= y
+    lo = hi - 1
+    dl, dh = y - E4M3_GRID[lo], E4M3_GRID[hi] - y
+    pick_hi = (dh < dl) | ((dh == dl) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(y == 0, 0, code)
+    r = np.sign(xb) * E4M3_GRID[code] * np.ldexp(1.0, s)
+    return r.reshape(xp.shape)[..., :n]
+
+
+def joint_attention_mx(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, sm_scale: float,
+                       with_bound: bool = False):
+    """The MXFP8 route for each head: q' = MXFP8(q) in blocks of 32 latent dims; key i is
+    scales[i] * codes[i] (a main entry: its exact latent with scale 1; a window token: its
+    E4M3 code values and fp32 scale); z_i = sm_scale * q' . key_i, p_i = exp(z_i - max z),
+    the weight on key i's codes w_i = p_i * scales[i] is rounded to MXFP8 in blocks of 32
+    consecutive keys, out = sum_i w'_i codes_i / sum_i p_i, lse = max z + log sum p.
+
+    with_bound: also return, per (head, dim), what two independent roundings of w to E4M3
+    (here and in an implementation that rounds w times a factor >= 1 and divides it out
+    later) can move out by.  One rounding moves a value by at most 2^-3 of itself in
+    E4M3's normal range (half a grid step is 2^-4 relative; a block maximum between 448
+    and 512 grid units saturates to 448, up to 1/8 below), and in the subnormal range by
+    at most 2^-10 * 2^s here and 2^-9 * 2^s there, so the bound is
+    sum_i (2^-2 |w_i| + 2^-8 * 2^s_i) |codes_i| / sum p.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    codes = np.asarray(codes, dtype=np.float64)
+    scales = np.asarray(scales, dtype=np.float64)
+    H = q.shape[0]
+    if codes.shape[0] == 0:
+        out = np.zeros((H, D))
+        lse = np.full(H, -np.inf)
+        return (out, lse, np.zeros((H, D))) if with_bound else (out, lse)
+    qm = mxfp8_round(q)
+    z = (qm @ codes.T) * scales[None, :] * float(sm_scale)          # [H, n]
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    l = p.sum(axis=1, keepdims=True)
+    w = p * scales[None, :]
+    wm = mxfp8_round(w)
+    out = (wm @ codes) / l
+    lse = (m + np.log(l))[:, 0]
+    if not with_bound:
+        return out, lse
+    n = w.shape[1]
+    nb = -(-n // 32)
+    wp = np.zeros((H, nb * 32))
+    wp[:, :n] = np.abs(w)
+    amax = wp.reshape(H, nb, 32).max(axis=2)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    step = np.ldexp(1.0, np.clip(e - 1 - 8, -127, 127) - 8)        # twice E4M3's subnormal step * 2^s
+    step = np.repeat(np.where(amax > 0, step, 0.0), 32, axis=1)[:, :n]
+    bound = ((2.0 ** -2) * np.abs(w) + step) @ np.abs(codes) / l
+    return out, lse, bound
+
+
+def row_key_codes(wl, r: int, sel: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """The row's attention keys as (codes, scales): the selected main entries' exact
+    latents with scale 1, then the window tokens' E4M3 code values and fp32 scales."""
+    b = int(wl.row_req[r])
+    sel = np.asarray(sel, dtype=np.int64)
+    sel = sel[(sel >= 0) & (sel < visible(wl, r))]
+    main = dequant_main(wl.main_kv[entry_rows(wl, b, sel)])
+    s0 = int(wl.row_swa_start[r])
+    s1 = s0 + int(wl.row_swa_len[r])
+    win = E4M3[np.asarray(wl.swa[s0:s1], dtype=np.int64)].reshape(-1, D)
+    codes = np.concatenate([main, win], axis=0)
+    scales = np.concatenate([np.ones(main.shape[0]), np.asarray(wl.swa_scale[s0:s1], dtype=np.float64)])
+    return codes, scales
+
+
+# ---------------------------------------------------------------------------------
 # The whole path for one workload.
 # ---------------------------------------------------------------------------------
 

@@ -22,6 +22,7 @@ D, HEADS, IDX_D, IDX_HEADS, BLOCK, SWA_MAX = 512, 64, 128, 8, 64, 128
 MAIN_BYTES, IDX_BYTES = 288, 68
 K_MAX, KEEP_MAX, ROWS_PER_REQ_MAX, TOPK_ALL_MAX = 2048, 128, 16, 8192
 DQ_MAIN, DQ_IDX, DQ_SWA = 0, 1, 2
+QP_BF16, QP_MXFP8 = 0, 1
 DECODE_EVENTS = 5
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = 0, 1, 2, 3, 4
@@ -57,13 +58,13 @@ class _DecodeArgs(ctypes.Structure):
         ("sel_idx", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
         ("kept_blocks", ctypes.c_void_p), ("n_kept", ctypes.c_void_p),
         ("scores", ctypes.c_void_p), ("scores_ld", ctypes.c_int64),
-        ("events", ctypes.c_void_p),
+        ("events", ctypes.c_void_p), ("qp_route", ctypes.c_int32),
     ]
 
 
 EXPORTS = ("csa2_index_score", "csa2_block_filter", "csa2_topk", "csa2_sparse_attn",
            "csa2_sparse_attn_workspace_size", "csa2_decode", "csa2_decode_workspace_size",
-           "csa2_debug_dequant", "csa2_debug_stream_read", "csa2_status_string", "csa2_last_error",
+           "csa2_debug_dequant", "csa2_debug_mxfp8", "csa2_debug_stream_read", "csa2_status_string", "csa2_last_error",
            "csa2_version")
 
 _lib = None
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "csa2_decode_workspace_size": ([DA], SZ),
         "csa2_debug_dequant": ([I32, P, P, I64, P, P], ctypes.c_int),
         "csa2_debug_stream_read": ([P, I64, P, P], ctypes.c_int),
+        "csa2_debug_mxfp8": ([P, I64, P, P], ctypes.c_int),
         "csa2_status_string": ([I32], ctypes.c_char_p),
         "csa2_last_error": ([], ctypes.c_char_p),
         "csa2_version": ([], I32),
@@ -274,7 +276,7 @@ class Decoder:
 
     def __init__(self, rg: Ragged, idx_k, main_kv, blk_sum, swa, swa_scale, q, q_idx, w_idx, k: int = 512,
                  n_keep: int = 64, keep_newest: bool = True, sm_scale: float = 1.0 / math.sqrt(D),
-                 scan_mode: int = 0, keep_intermediates: bool = True):
+                 scan_mode: int = 0, keep_intermediates: bool = True, qp_route: int = QP_BF16):
         lib = load_library()
         for t, dts, n in ((idx_k, (torch.uint8,), "idx_k"), (main_kv, (torch.uint8,), "main_kv"),
                           (blk_sum, _BF16, "blk_sum"), (swa, (torch.uint8,), "swa"),
@@ -299,6 +301,7 @@ class Decoder:
         a.idx_k, a.main_kv, a.blk_sum = _ptr(idx_k), _ptr(main_kv), _ptr(blk_sum)
         a.swa, a.swa_scale, a.q, a.q_idx, a.w_idx = _ptr(swa), _ptr(swa_scale), _ptr(q), _ptr(q_idx), _ptr(w_idx)
         a.k, a.n_keep, a.keep_newest, a.scan_mode = k, n_keep, 1 if keep_newest else 0, scan_mode
+        a.qp_route = qp_route
         a.sm_scale = float(sm_scale)
         a.out, a.lse = _ptr(self.out), _ptr(self.lse)
         a.sel_idx, a.n_sel = _ptr(self.sel_idx), _ptr(self.n_sel)
@@ -356,6 +359,15 @@ def debug_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
     _dev(sink, (torch.int32,), "sink")
     nbytes = src.numel() * src.element_size()
     _check(lib.csa2_debug_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream()))
+
+
+def debug_mxfp8(x: torch.Tensor) -> torch.Tensor:
+    """The attention kernel's MXFP8 rounding over fp32 ``x`` in blocks of 32 values."""
+    lib = load_library()
+    _dev(x, (torch.float32,), "x")
+    out = torch.empty_like(x)
+    _check(lib.csa2_debug_mxfp8(_ptr(x), x.numel(), _ptr(out), _stream()))
+    return out
 
 
 def debug_dequant(kind: int, records: torch.Tensor, scales: torch.Tensor | None = None) -> torch.Tensor:

@@ -175,6 +175,28 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hi
   return hipGetLastError();
 }
 
+// Test hook: lane (i, g) of a wave rounds values 8g .. 8g+7 of block 16w + i (w = the
+// wave's index in the grid) with the attention kernel's block helper.
+__global__ __launch_bounds__(256) void k_debug_mxfp8(const float* x, int64_t nblocks, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + (lane & 15);
+  const int g = lane >> 4;
+  const bool ok = blk < nblocks;
+  float v[8];
+  for (int j = 0; j < 8; ++j) v[j] = ok ? x[blk * 32 + 8 * g + j] : 0.f;
+  float r[8];
+  bf16x8_words_to_f32(mx8_round_block_bf16x8(v), r);
+  if (ok)
+    for (int j = 0; j < 8; ++j) out[blk * 32 + 8 * g + j] = r[j];
+}
+
+hipError_t launch_debug_mxfp8(const float* x, int64_t n, float* out, hipStream_t st) {
+  const int64_t nblocks = n / 32;
+  if (nblocks == 0) return hipSuccess;
+  k_debug_mxfp8<<<dim3((unsigned)ceil_div(nblocks, 64)), dim3(256), 0, st>>>(x, nblocks, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
                                 hipStream_t st) {
   const int groups = (kind == CSA2_DQ_IDX) ? CSA2_IDX_D / 8 : CSA2_D / 8;
@@ -415,6 +437,8 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   if (a->n_keep < 1 || a->n_keep > CSA2_KEEP_MAX)
     return fail(CSA2_ERR_UNSUPPORTED, "n_keep must be in 1..%d", CSA2_KEEP_MAX);
   if (a->scan_mode != 0 && a->scan_mode != 1) return fail(CSA2_ERR_UNSUPPORTED, "scan_mode must be 0 or 1");
+  if (a->qp_route != CSA2_QP_BF16 && a->qp_route != CSA2_QP_MXFP8)
+    return fail(CSA2_ERR_UNSUPPORTED, "qp_route must be CSA2_QP_BF16 or CSA2_QP_MXFP8");
   if (g.R == 0) return CSA2_OK;
   CHECK(check_ptr(a->idx_k, 4, "idx_k"));
   CHECK(check_ptr(a->blk_sum, 16, "blk_sum"));
@@ -445,6 +469,7 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   CHECK(attn_args(g, a->q, a->main_kv, sel_rows ? sel_rows : sel, n_sel, a->k, a->swa, a->swa_scale, a->sm_scale,
                   a->out, a->lse, attn_ws, attn_bytes, at));
   at.sel_rows = sel_rows ? 1 : 0;
+  at.qp_route = a->qp_route;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   ScanArgs sa{};
@@ -512,6 +537,16 @@ int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales
   CHECK(check_ptr(out, 4, "out"));
   if (kind == CSA2_DQ_SWA) CHECK(check_ptr(scales, 4, "scales"));
   LAUNCH(launch_debug_dequant(kind, records, scales, n, out, reinterpret_cast<hipStream_t>(stream)), "dequant");
+  return CSA2_OK;
+}
+
+int csa2_debug_mxfp8(const float* x, int64_t n, float* out, void* stream) {
+  if (n < 0 || n % 32 != 0) return fail(CSA2_ERR_INVALID_ARG, "n must be a non-negative multiple of 32");
+  if (n == 0) return CSA2_OK;
+  if (n / 32 / 64 >= (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_UNSUPPORTED, "too many values for one launch");
+  CHECK(check_ptr(x, 4, "x"));
+  CHECK(check_ptr(out, 4, "out"));
+  LAUNCH(launch_debug_mxfp8(x, n, out, reinterpret_cast<hipStream_t>(stream)), "mxfp8 rounding");
   return CSA2_OK;
 }
 

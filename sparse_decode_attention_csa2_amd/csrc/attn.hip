@@ -116,6 +116,9 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 // each wave contracts its half of the dims for S^T = K Q^T and the two halves meet
 // through LDS; the online softmax runs identically in both waves of a head group; PV
 // reads its A operand (V^T) from the same key-major copy with transposing LDS loads.
+// MX: the MXFP8 route (Q and P rounded to MXFP8 before their products); otherwise Q as
+// given and P as exact-to-2^-17 bf16 hi + lo parts.
+template <bool MX>
 __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   constexpr int TK = kAttnTileKeys;   // 64
   constexpr int KB = TK / 32;         // 32-key groups
@@ -197,6 +200,16 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     for (int st = 0; st < 8; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
   }
   load_keys(k_begin);
+  if constexpr (MX) {
+    // MXFP8 route: block st of 32 dims = this lane's 8 values and those of lanes xor 16
+    // and xor 32 (rounded while the first tile's records are in flight).
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      float v[8];
+      bf16x8_words_to_f32(qb[st], v);
+      qb[st] = mx8_round_block_bf16x8(v);
+    }
+  }
 
   // Transposed-read offsets (elements): lane (g, i = 4k + q) points at key 4g + k of a
   // 16-key half and dims 4q .. 4q+3 of a 16-dim tile.
@@ -267,7 +280,10 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
     // Probabilities enter PV as bf16 hi + lo parts: one bf16 would round each weight
-    // by up to 2^-9 relative, the whole error budget of the output.
+    // by up to 2^-9 relative, the whole error budget of the output.  MX route: each
+    // 32-key group's weights (p times the key's window scale, the factor on its stored
+    // codes) are rounded to MXFP8, which is exact in one bf16; the normaliser keeps the
+    // unrounded p.
     float psum = 0.f;
     bf16x8_t pb_hi[KB], pb_lo[KB];
 #pragma unroll
@@ -280,7 +296,10 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
         psum += p;
         pv[j] = p * sc[zi];
       }
-      split_bf16x8(pv, pb_hi[c], pb_lo[c]);
+      if constexpr (MX)
+        pb_hi[c] = mx8_round_block_bf16x8(pv);
+      else
+        split_bf16x8(pv, pb_hi[c], pb_lo[c]);
     }
     l_run = l_run * alpha + psum;
     // Rescale the accumulators only when a head's running maximum moved.
@@ -308,8 +327,10 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[t0 + v] = mfma16x16x32(av[v], pb_hi[c], o[t0 + v]);
+        if constexpr (!MX) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[t0 + v] = mfma16x16x32(av[v], pb_lo[c], o[t0 + v]);
+          for (int v = 0; v < 4; ++v) o[t0 + v] = mfma16x16x32(av[v], pb_lo[c], o[t0 + v]);
+        }
       }
     }
     __syncthreads();   // LDS reads of this tile are done before the next tile's writes
@@ -426,7 +447,10 @@ size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
 
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  k_attn<<<dim3(a.splits, a.g.R), dim3(512), 0, st>>>(a);
+  if (a.qp_route == CSA2_QP_MXFP8)
+    k_attn<true><<<dim3(a.splits, a.g.R), dim3(512), 0, st>>>(a);
+  else
+    k_attn<false><<<dim3(a.splits, a.g.R), dim3(512), 0, st>>>(a);
   return hipGetLastError();
 }
 

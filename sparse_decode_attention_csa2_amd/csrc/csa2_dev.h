@@ -69,6 +69,45 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8_t& hi, 
   lo = __builtin_bit_cast(bf16x8_t, lw);
 }
 
+// ---------------------------------------------------------------------------------
+// MXFP8 (OCP MX v1.0: E4M3 elements sharing one E8M0 scale per 32-value block).
+// The block's shared exponent is floor(log2(amax)) - 8 (E4M3's largest exponent),
+// clamped to E8M0's range; each value x becomes RNE_E4M3(x / 2^s) * 2^s, saturating at
+// 448.  The rounding is done in fp32 arithmetic (exact scalings, one round-to-nearest-
+// even of a value with the grid step brought to 1), not by a conversion instruction.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ int mx8_scale_exp(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1;   // floor(log2(amax)), subnormals included
+  const int s = e - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+__device__ __forceinline__ float mx8_round(float x, int s) {
+  const float y = fminf(__builtin_ldexpf(fabsf(x), -s), 448.f);   // |x| / 2^s, < 2^9
+  // Grid step 2^(e-3) with e = floor(log2 y), and 2^-9 (subnormals) below 2^-6.
+  const int e = max(__builtin_amdgcn_frexp_expf(y) - 1, -6);
+  const float r = __builtin_ldexpf(__builtin_rintf(__builtin_ldexpf(y, 3 - e)), e - 3);
+  return copysignf(__builtin_ldexpf(fminf(r, 448.f), s), x);
+}
+
+// MXFP8-round 8 fp32 values of a 32-value block whose other 24 values sit in the lanes
+// xor 16 and xor 32 (a lane's 8 values are one quarter of the block), packed as an exact
+// bf16 MFMA operand (element q in the low half of word q / 2).
+__device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  const int s = mx8_scale_exp(amax);
+  u32x4_t w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    w[q] = bf16_bits_rne(mx8_round(v[2 * q], s)) | (bf16_bits_rne(mx8_round(v[2 * q + 1], s)) << 16);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 // Widen 8 bf16 to fp32 through the packed 32-bit words (integer shifts only).
 __device__ __forceinline__ void bf16x8_words_to_f32(bf16x8_t x, float (&v)[8]) {
   const u32x4_t w = __builtin_bit_cast(u32x4_t, x);

@@ -160,6 +160,7 @@ struct AttnArgs {
   const int32_t* n_sel;
   int32_t sel_ld;
   int32_t sel_rows;
+  int32_t qp_route;          // CSA2_QP_BF16 or CSA2_QP_MXFP8
   const uint8_t* swa;
   const float* swa_scale;
   float sm_scale_log2;       // sm_scale * log2(e)
@@ -183,6 +184,7 @@ hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
 hipError_t launch_sel_rows(const RaggedDev& g, const int32_t* sel, const int32_t* n_sel, int32_t sel_ld,
                            int32_t* rows, hipStream_t st);
 
+hipError_t launch_debug_mxfp8(const float* x, int64_t n, float* out, hipStream_t st);
 hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
                                 hipStream_t st);
 

@@ -386,16 +386,18 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_ent
   float* ss = a.sel_score ? a.sel_score + (int64_t)r * k : nullptr;
   auto pos_of = [&](int i) { return (int64_t)sh.kl[i / CSA2_BLOCK] * CSA2_BLOCK + (i % CSA2_BLOCK); };
   const int nk_c = nk > 0 ? nk : 1;   // slot index clamp for unconditional reads
-  // Pool rows of the picks (attention over paged pools): the page of each kept block
-  // is looked up once here, so the emit below translates from LDS.
+  // Pool rows of the picks (attention over paged pools): thread s looks up the page of
+  // kept block s (nk <= 129 < NT) once, with its load in flight together with the
+  // gather's, and the emit below translates from LDS.
+  static_assert(CSA2_KEEP_MAX + 1 <= NT, "one kept block per thread");
   int32_t* rows = (PAGED && a.sel_rows && !all_entries) ? a.sel_rows + (int64_t)r * k : nullptr;
-  if (PAGED && rows) {
-    const int b = row_request(a.g, r);
-    for (int s = threadIdx.x; s < nk; s += NT) {
-      const int64_t kb = sh.kl[s];
-      const bool ok = kb >= 0 && kb * CSA2_BLOCK < n;
-      sh.kpage[s] = ok ? (int32_t)(page_of(a.g, b, kb) * CSA2_BLOCK) : 0;
-    }
+  int32_t kpage = 0;
+  if (PAGED && rows && (int)threadIdx.x < nk) {
+    const int64_t kb = sh.kl[threadIdx.x];
+    const bool ok = kb >= 0 && kb * CSA2_BLOCK < n;
+    const int64_t lp = ok ? kb : 0;   // an in-range page-table slot either way
+    const int64_t pg = page_of(a.g, row_request(a.g, r), lp) * CSA2_BLOCK;
+    kpage = ok ? (int32_t)pg : 0;
   }
   int items;
   if (all_entries) {
@@ -413,6 +415,7 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_ent
     };
     gather(items, valid, [&](int i, bool ok) { return sc[ok ? slot_pos(i) : 0]; }, kbuf, sh);
   }
+  if (PAGED && rows && (int)threadIdx.x < nk) sh.kpage[threadIdx.x] = kpage;
   __syncthreads();
   const int take = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), k, sh, [&](int pos, int i) {
     sel[pos] = all_entries ? i : (int32_t)pos_of(i);

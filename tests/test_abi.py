@@ -21,7 +21,7 @@ def lib():
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "csa2.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):

@@ -391,3 +391,71 @@ def test_paged_pools_match_contiguous():
     pw.page_table[1, [0, 1]] = pw.page_table[1, [1, 0]]
     c = oracle.decode(pw, rows=[1], k=300, n_keep=16)[0]
     assert not np.array_equal(c["scores"], a[1]["scores"])
+
+
+# ---------------------------------------------------------------------------------
+# MXFP8 route.
+# ---------------------------------------------------------------------------------
+
+def _mx_reference(x):
+    """Independent MXFP8 rounding of one 32-value block: shared exponent from frexp,
+    elements through torch's float8_e4m3fn conversion (round to nearest even), values
+    above 448 clamped first (saturation)."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max()
+    if amax == 0:
+        return np.zeros_like(x)
+    s = max(-127, min(127, int(np.floor(np.log2(amax))) - 8))
+    y = np.clip(x / 2.0 ** s, -448.0, 448.0)
+    e = torch.from_numpy(y).to(torch.float8_e4m3fn).double().numpy()
+    return e * 2.0 ** s
+
+
+def test_mxfp8_round_matches_torch_e4m3():
+    rng = np.random.default_rng(11)
+    blocks = []
+    for mag in (1e-30, 1e-6, 2.0 ** -20, 0.1, 1.0, 3.7, 448.0, 1e5, 2.0 ** 100):
+        for _ in range(20):
+            blocks.append(rng.standard_normal(32) * mag)
+    b = rng.standard_normal(32)
+    b[3] = 0.0
+    b[5] = b.max() * 1e-6                      # deep in E4M3's subnormal range
+    blocks.append(b)
+    blocks.append(np.zeros(32))
+    x = np.stack(blocks)
+    got = oracle.mxfp8_round(x)
+    ref = np.stack([_mx_reference(v) for v in x])
+    assert np.array_equal(got, ref)
+
+
+def test_mxfp8_round_closed_forms():
+    # Block max 500: scale 2^0.  Ties go to the even code; above 448 saturates.
+    x = np.zeros(32)
+    x[:9] = [17.0, 19.0, 300.0, 500.0, 460.0, -17.0, 0.0009765625, 0.00146484375, 0.5]
+    got = oracle.mxfp8_round(x)[:9]
+    assert got.tolist() == [16.0, 20.0, 288.0, 448.0, 448.0, -16.0, 0.0, 0.001953125, 0.5]
+    # Values already on an MX grid are unchanged; a scale of 2^k leaves the codes alone.
+    y = oracle.mxfp8_round(np.linspace(-3, 3, 64))
+    assert np.array_equal(oracle.mxfp8_round(y), y)
+    assert np.array_equal(oracle.mxfp8_round(y * 2.0 ** 40), y * 2.0 ** 40)
+    # Partial last block is padded for the scale only.
+    assert oracle.mxfp8_round(np.array([1.0, 17.0])).tolist() == [1.0, 16.0]
+
+
+def test_mx_attention_closed_forms_and_bound():
+    rng = np.random.default_rng(12)
+    codes = oracle.E2M1[rng.integers(0, 16, size=(70, 512))]
+    # Equal logits (q = 0): p = 1 everywhere, MXFP8(1) = 1, so out is the plain mean.
+    q = np.zeros((64, 512))
+    out, lse = oracle.joint_attention_mx(q, codes, np.ones(70), 0.05)
+    assert np.allclose(out, codes.mean(axis=0)[None, :], rtol=0, atol=1e-12)
+    assert np.allclose(lse, np.log(70.0))
+    # With unrounded Q and P the route is the plain attention; rounding moves the output
+    # by no more than the bound it reports.
+    q = oracle.mxfp8_round(rng.standard_normal((64, 512)))   # already on the MX grid
+    sc = np.ones(70)
+    o1, l1, bound = oracle.joint_attention_mx(q, codes, sc, 0.04, with_bound=True)
+    o0, l0 = oracle.joint_attention(q, codes, 0.04)
+    assert np.allclose(l1, l0, rtol=0, atol=1e-12)
+    assert np.all(np.abs(o1 - o0) <= bound / 2 + 1e-12)
+    assert np.abs(o1 - o0).max() > 0        # P really is rounded
