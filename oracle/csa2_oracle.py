@@ -49,6 +49,9 @@ and translates positions into KV page addresses.  Read here as:
                    then at row 64 * page_table[b][t // 64] + t % 64 and its block's
                    summary at row page_table[b][t // 64].
 
+[KT] contrasts full-BF16 sparse MLA with a route that rounds Q and P to MXFP8 (OCP MX:
+E4M3 elements, one E8M0 scale per 32 values); joint_attention_mx states that route.
+
 Every function here is pinned by tests in tests/test_formats.py and tests/test_oracle.py
 (format tables against a library decoder and the OCP MX value table, brute-force exact
 rational scores, brute-force selection, the dense-attention special case, LSE merging
