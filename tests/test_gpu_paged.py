@@ -171,3 +171,35 @@ def test_standalone_entry_points_paged_equal_contiguous(csa2):
         ro, rl = oracle.joint_attention(oracle.bf16_value(wl.q[r]), oracle.row_keys(wl, r, sel_np[r]), wl.sm_scale)
         rel, dl = parity.attn_error(oa[r].cpu().numpy(), la[r].cpu().numpy(), ro, rl)
         assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS, (r, rel, dl)
+
+
+def test_out_of_range_page_ids_are_clamped(csa2):
+    # Page ids outside 0 .. total_pages-1 address the nearest valid page (the documented
+    # clamp): the result equals a decode whose page table holds the clamped ids.  Whole
+    # pages and no spare pages, so every page holds real records (no random bytes).
+    pw = to_paged(make_workload("clamp", 47, [64 * 30, 64 * 14], rows_per_req=[2, 1], n_needles=4),
+                  spare_pages=0)
+    bad = pw.page_table.copy()
+    bad[0, 3] = -5
+    bad[1, 2] = pw.total_pages + 100
+    clamped = np.clip(bad, 0, pw.total_pages - 1)
+    pw.page_table = bad
+    got = run_decode(csa2, pw, k=200, n_keep=16)
+    pw.page_table = clamped
+    ref = run_decode(csa2, pw, k=200, n_keep=16)
+    for key in ("sel", "kept", "out", "lse"):
+        assert same(got[key], ref[key]), key
+    judge(pw, got, k=200, n_keep=16)
+
+
+def test_sixteen_rows_per_request_paged_with_row_len(csa2):
+    # The largest row group (16 rows share one key stream: the 8-pair scan), paged, with
+    # every row seeing a different prefix, in both scan modes.
+    wl = make_workload("rows16", 48, [64 * 70 + 33, 5000], rows_per_req=[16, 3], n_needles=8)
+    rl = np.array([64 * 70 + 33 - 37 * j for j in range(16)] + [5000, 64, 4999], dtype=np.int64)
+    wl.row_len = rl
+    pw = to_paged(wl)
+    _log("16 rows per request, paged, row lengths")
+    for scan_mode in (0, 1):
+        got = run_decode(csa2, pw, k=256, n_keep=24, scan_mode=scan_mode)
+        judge(pw, got, k=256, n_keep=24)
