@@ -99,6 +99,33 @@ def graph_time_ms(hip, fns, replays: int, warm: int = 2) -> float:
     return elapsed_ms(hip, ev[0], ev[1]) / (replays * len(fns))
 
 
+def cache_write_timing(csa2, hip) -> dict:
+    """csa2_cache_write (pooling, RMSNorm, FP4 quantisation, record and summary writes)
+    for the verify batch (8 requests x 6 rows) and for 64 requests x 2 rows, graph-timed."""
+    import torch
+    from synth import make_config, make_write_inputs
+    from synth.device import upload
+    out = {}
+    for name, wl in (("verify_8x6", make_config(3)), ("decode_64x2", None)):
+        if wl is None:
+            from synth import make_workload
+            wl = make_workload("decode_64x2", 7, [4096] * 64, rows_per_req=2, n_needles=0)
+        w = make_write_inputs(wl, 70)
+        dw = upload(wl)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                                         else np.ascontiguousarray(a)).cuda()
+        args = (dw.rg, dev(w["row_pos"]), dev(w["kv_tok"]), dev(w["idx_tok"]), dev(w["ring_kv"]), dev(w["ring_idx"]),
+                dev(w["gamma_kv"]), dev(w["gamma_idx"]), dw.main_kv, dw.idx_k, dw.blk_sum)
+        csa2.cache_write(*args)
+        torch.cuda.synchronize()
+        ms = graph_time_ms(hip, [lambda: csa2.cache_write(*args)], replays=200)
+        entries = int(sum(1 for p in w["row_pos"] if p % 2 == 1))
+        out[name] = {"rows": wl.num_rows, "entries_written": entries, "us_per_call": ms * 1e3}
+        del dw, args
+        torch.cuda.empty_cache()
+    return out
+
+
 def touched_bytes(wl) -> int:
     """Bytes a decode step reads from the pools (for sizing the replica rotation)."""
     R = wl.num_rows
@@ -482,6 +509,7 @@ def main() -> int:
             del mi, w
             torch.cuda.empty_cache()
         res["per_config"] = per
+        res["cache_write"] = cache_write_timing(csa2, hip)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

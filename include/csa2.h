@@ -233,6 +233,35 @@ typedef struct csa2_decode_args {
 int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_decode_workspace_size(const csa2_decode_args* a);
 
+/*
+ * Cache write (the step before the path; SGLang blog, section "Small-operator fusion and
+ * GEMV": pooling, RMSNorm, FP4 quantisation and the cache write run as one fused chain;
+ * section "DSpark adaptation and optimization": verify positions are contiguous, so a
+ * row's pooling partner is the previous row, and only the first row of a request needs
+ * the ring buffer).  Row r is a new token at position row_pos[r] of its request (the
+ * rows of a request hold consecutive positions); kv_tok[r] (512) and idx_tok[r] (128)
+ * are its compressor outputs, bf16.  Global entry t pools tokens 2t and 2t+1, so a row
+ * at an odd position P completes entry t = (P-1)/2:
+ *   pooled = (x[P-1] + x[P]) / 2, x[P-1] = the previous row of the request if it holds
+ *            position P-1, else the request's ring slot (ring_kv[b], ring_idx[b]);
+ *   y      = pooled * gamma / sqrt(mean(pooled^2) + eps)     (per vector, fp32);
+ *   record = OCP MX FP4 of y: per block (16 dims main, 32 dims index) the E8M0 exponent
+ *            floor(log2(block amax)) - 2 (0 for an all-zero block: scale byte 0),
+ *            elements y / 2^e rounded to the nearest E2M1 value (ties to the even code,
+ *            6 for everything above 5), laid out as in the formats above;
+ * and writes the main and index records of entry t at its pool row (t < N_b required;
+ * other rows write nothing).  Then, for every block that received an entry, the
+ * summary = bf16 (round to nearest even) of the mean of the dequantised index keys of
+ * the block's entries 0 .. min(63, N_b - 1 - 64j); and a request whose last row sits at
+ * an even position stores that row's vectors in its ring slot.  row_len and sel-related
+ * fields of rg are ignored; N_b = entry_off[b+1] - entry_off[b] already counts the new
+ * entries.  gamma_kv [512] / gamma_idx [128] fp32; eps > 0.  The ring slots are read
+ * before any is written.  Rows whose position is negative are skipped.
+ */
+int csa2_cache_write(const csa2_ragged* rg, const int64_t* row_pos, const uint16_t* kv_tok, const uint16_t* idx_tok,
+                     uint16_t* ring_kv, uint16_t* ring_idx, const float* gamma_kv, const float* gamma_idx, float eps,
+                     uint8_t* main_kv, uint8_t* idx_k, uint16_t* blk_sum, void* stream);
+
 /* Test hook: run the kernels' own dequantisation helpers over raw records.
  * kind CSA2_DQ_MAIN: records [n][288] -> out [n][512]; CSA2_DQ_IDX: [n][68] -> [n][128];
  * CSA2_DQ_SWA: records [n][512] E4M3FN with scales [n] -> out [n][512] = fp32(x * scale).

@@ -228,6 +228,109 @@ def joint_attention(q: np.ndarray, keys: np.ndarray, sm_scale: float) -> tuple[n
 
 
 # ---------------------------------------------------------------------------------
+# O8. The cache write (the step before the path): [SGL] "Small-operator fusion and
+# GEMV" fuses pooling, RMSNorm, FP4 quantisation and the cache write; "DSpark
+# adaptation and optimization": verify rows pool with the previous row, only a
+# request's first row reads the ring buffer, and the same write serves index K.
+# ---------------------------------------------------------------------------------
+
+E2M1_GRID = E2M1[:8]            # magnitudes of codes 0 .. 7: 0, .5, 1, 1.5, 2, 3, 4, 6
+
+
+def fp4_encode(y: np.ndarray, block: int) -> tuple[np.ndarray, np.ndarray]:
+    """OCP MX FP4 of each row of y [n, dim]: per block the E8M0 exponent
+    e = floor(log2(block amax)) - 2 (E2M1's largest exponent; -127 for an all-zero
+    block), clamped to -127 .. 127; each element the E2M1 code nearest to y / 2^e (ties to
+    the even code, magnitudes above 6 to 6).  Returns (codes [n, dim] uint8, exponents
+    [n, dim/block] int)."""
+    y = np.asarray(y, dtype=np.float64)
+    n, dim = y.shape
+    yb = y.reshape(n, dim // block, block)
+    amax = np.abs(yb).max(axis=2)
+    _, fe = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.where(amax > 0, np.clip(fe - 1 - 2, -127, 127), -127)
+    v = np.abs(yb) / np.ldexp(1.0, e)[..., None]
+    d = np.abs(v[..., None] - E2M1_GRID)                          # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    ties = d == best
+    # Among equally near magnitudes take the even code (codes are 0..7, ascending).
+    even = ties & (np.arange(8) % 2 == 0)
+    mag = np.where(even.any(axis=-1), even.argmax(axis=-1), ties.argmax(axis=-1))
+    sign = (yb < 0) & (mag > 0)
+    codes = (mag | (sign.astype(np.int64) << 3)).reshape(n, dim).astype(np.uint8)
+    return codes, e.astype(np.int64)
+
+
+def pack_fp4_record(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """Records of the stored layout: element 2i in the low nibble of byte i, then the
+    E8M0 bytes e + 127."""
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return np.concatenate([packed, (exps + 127).astype(np.uint8)], axis=1)
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of fp64 values, one round to nearest even (normal range)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                                          # x = m 2^e, |m| in [0.5, 1)
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)               # 8 significant bits
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x * gamma / sqrt(mean(x^2) + eps) per row."""
+    x = np.asarray(x, dtype=np.float64)
+    return x * np.asarray(gamma, dtype=np.float64) / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+
+
+def cache_write(wl, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, eps: float = 1e-6) -> dict:
+    """The cache write on copies of wl's pools.  Row r (a token at position row_pos[r];
+    a request's rows hold consecutive positions) at an odd position P completes entry
+    t = (P-1)/2 of its request if t < N_b: pooled = mean of the token at P-1 (the previous
+    row if it holds P-1, else the request's ring slot) and the row's own token; main and
+    index vectors each go through rms_norm and fp4_encode (blocks 16 / 32) into the
+    entry's records.  Each block that received an entry gets as summary the bf16 of the
+    mean of its entries' dequantised index keys; a request whose last row has an even
+    position moves that row's tokens into its ring slot.  Returns the updated pools and
+    ring slots plus, per written entry, the normalised vectors ``y_kv`` / ``y_idx``."""
+    main = np.array(wl.main_kv, copy=True)
+    idx = np.array(wl.idx_k, copy=True)
+    summ = np.array(wl.blk_sum, copy=True)
+    rkv = np.array(ring_kv, copy=True)
+    ridx = np.array(ring_idx, copy=True)
+    written = {}
+    for b in range(wl.num_requests):
+        r0, r1 = int(wl.row_off[b]), int(wl.row_off[b + 1])
+        n = int(wl.entry_off[b + 1] - wl.entry_off[b])
+        ts = []
+        for r in range(r0, r1):
+            p = int(row_pos[r])
+            if p < 0 or p % 2 == 0 or (p - 1) // 2 >= n:
+                continue
+            t = (p - 1) // 2
+            if r > r0 and int(row_pos[r - 1]) == p - 1:
+                pk, pi = kv_tok[r - 1], idx_tok[r - 1]
+            else:
+                pk, pi = ring_kv[b], ring_idx[b]
+            xk = (bf16_value(pk) + bf16_value(kv_tok[r])) / 2
+            xi = (bf16_value(pi) + bf16_value(idx_tok[r])) / 2
+            yk = rms_norm(xk[None, :], gamma_kv, eps)
+            yi = rms_norm(xi[None, :], gamma_idx, eps)
+            row = int(entry_rows(wl, b, np.array([t]))[0])
+            main[row] = pack_fp4_record(*fp4_encode(yk, 16))[0]
+            idx[row] = pack_fp4_record(*fp4_encode(yi, 32))[0]
+            written[(b, t)] = (yk[0], yi[0])
+            ts.append(t)
+        for j in sorted(set(t // BLOCK for t in ts)):
+            cnt = min(BLOCK, n - BLOCK * j)
+            keys = dequant_idx(idx[entry_rows(wl, b, np.arange(BLOCK * j, BLOCK * j + cnt))])
+            summ[int(block_rows(wl, b, j + 1)[j])] = bf16_rne(keys.mean(axis=0))
+        if r1 > r0 and int(row_pos[r1 - 1]) >= 0 and int(row_pos[r1 - 1]) % 2 == 0:
+            rkv[b] = kv_tok[r1 - 1]
+            ridx[b] = idx_tok[r1 - 1]
+    return dict(main_kv=main, idx_k=idx, blk_sum=summ, ring_kv=rkv, ring_idx=ridx, written=written)
+
+
+# ---------------------------------------------------------------------------------
 # O7b. The MXFP8 Q/P route of the attention ([KT]: sparse MLA with Q and P rounded to
 # MXFP8 instead of full BF16).
 # ---------------------------------------------------------------------------------

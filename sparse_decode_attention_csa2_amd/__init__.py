@@ -62,7 +62,7 @@ class _DecodeArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("csa2_index_score", "csa2_block_filter", "csa2_topk", "csa2_sparse_attn",
+EXPORTS = ("csa2_index_score", "csa2_block_filter", "csa2_topk", "csa2_sparse_attn", "csa2_cache_write",
            "csa2_sparse_attn_workspace_size", "csa2_decode", "csa2_decode_workspace_size",
            "csa2_debug_dequant", "csa2_debug_mxfp8", "csa2_debug_stream_read", "csa2_status_string", "csa2_last_error",
            "csa2_version")
@@ -92,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "csa2_debug_dequant": ([I32, P, P, I64, P, P], ctypes.c_int),
         "csa2_debug_stream_read": ([P, I64, P, P], ctypes.c_int),
         "csa2_debug_mxfp8": ([P, I64, P, P], ctypes.c_int),
+        "csa2_cache_write": ([RG, P, P, P, P, P, P, P, F32, P, P, P, P], ctypes.c_int),
         "csa2_status_string": ([I32], ctypes.c_char_p),
         "csa2_last_error": ([], ctypes.c_char_p),
         "csa2_version": ([], I32),
@@ -359,6 +360,32 @@ def debug_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
     _dev(sink, (torch.int32,), "sink")
     nbytes = src.numel() * src.element_size()
     _check(lib.csa2_debug_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream()))
+
+
+def cache_write(rg: Ragged, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, main_kv, idx_k,
+                blk_sum, eps: float = 1e-6) -> None:
+    """csa2_cache_write: pool, normalise, quantise and write the entries the rows complete
+    (pools, summaries and ring slots are updated in place)."""
+    lib = load_library()
+    _dev(row_pos, (torch.int64,), "row_pos")
+    _dev(kv_tok, _BF16, "kv_tok")
+    _dev(idx_tok, _BF16, "idx_tok")
+    _dev(ring_kv, _BF16, "ring_kv")
+    _dev(ring_idx, _BF16, "ring_idx")
+    _dev(gamma_kv, (torch.float32,), "gamma_kv")
+    _dev(gamma_idx, (torch.float32,), "gamma_idx")
+    _dev(main_kv, (torch.uint8,), "main_kv")
+    _dev(idx_k, (torch.uint8,), "idx_k")
+    _dev(blk_sum, _BF16, "blk_sum")
+    if row_pos.numel() != rg.num_rows or kv_tok.numel() != rg.num_rows * D or idx_tok.numel() != rg.num_rows * IDX_D:
+        raise ValueError("row_pos / kv_tok / idx_tok do not match the rows of rg")
+    if ring_kv.numel() < rg.num_requests * D or ring_idx.numel() < rg.num_requests * IDX_D:
+        raise ValueError("ring slots must hold one token per request")
+    if gamma_kv.numel() != D or gamma_idx.numel() != IDX_D:
+        raise ValueError("gamma_kv must hold 512 values and gamma_idx 128")
+    _check(lib.csa2_cache_write(ctypes.byref(rg.c()), _ptr(row_pos), _ptr(kv_tok), _ptr(idx_tok), _ptr(ring_kv),
+                                _ptr(ring_idx), _ptr(gamma_kv), _ptr(gamma_idx), float(eps), _ptr(main_kv), _ptr(idx_k),
+                                _ptr(blk_sum), _stream()))
 
 
 def debug_mxfp8(x: torch.Tensor) -> torch.Tensor:

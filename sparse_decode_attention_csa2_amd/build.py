@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libcsa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["scan.hip", "select.hip", "attn.hip", "api.hip"]
+SOURCES = ["scan.hip", "select.hip", "attn.hip", "write.hip", "api.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

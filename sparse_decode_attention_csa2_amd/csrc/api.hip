@@ -540,6 +540,29 @@ int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales
   return CSA2_OK;
 }
 
+int csa2_cache_write(const csa2_ragged* rg, const int64_t* row_pos, const uint16_t* kv_tok, const uint16_t* idx_tok,
+                     uint16_t* ring_kv, uint16_t* ring_idx, const float* gamma_kv, const float* gamma_idx, float eps,
+                     uint8_t* main_kv, uint8_t* idx_k, uint16_t* blk_sum, void* stream) {
+  RaggedDev g;
+  CHECK(check_ragged(rg, g));
+  if (g.R == 0) return CSA2_OK;
+  if (!(eps > 0.f) || !isfinite(eps)) return fail(CSA2_ERR_INVALID_ARG, "eps must be positive and finite");
+  CHECK(check_ptr(row_pos, 8, "row_pos"));
+  CHECK(check_ptr(kv_tok, 16, "kv_tok"));
+  CHECK(check_ptr(idx_tok, 4, "idx_tok"));
+  CHECK(check_ptr(ring_kv, 16, "ring_kv"));
+  CHECK(check_ptr(ring_idx, 4, "ring_idx"));
+  CHECK(check_ptr(gamma_kv, 4, "gamma_kv"));
+  CHECK(check_ptr(gamma_idx, 4, "gamma_idx"));
+  CHECK(check_ptr(main_kv, 16, "main_kv"));
+  CHECK(check_ptr(idx_k, 4, "idx_k"));
+  CHECK(check_ptr(blk_sum, 4, "blk_sum"));
+  LAUNCH(launch_cache_write(g, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, eps, main_kv, idx_k,
+                            blk_sum, reinterpret_cast<hipStream_t>(stream)),
+         "cache write");
+  return CSA2_OK;
+}
+
 int csa2_debug_mxfp8(const float* x, int64_t n, float* out, void* stream) {
   if (n < 0 || n % 32 != 0) return fail(CSA2_ERR_INVALID_ARG, "n must be a non-negative multiple of 32");
   if (n == 0) return CSA2_OK;

@@ -1,0 +1,229 @@
+// Cache write on gfx950: pair pooling, RMSNorm, FP4/E8M0 quantisation, main-KV and
+// index-K record writes, block-summary update, ring-slot update.
+//
+// SGLang blog "DeepSeek-V4.1 Flash on SGLang", section "Small-operator fusion and
+// GEMV" (pooling, RMSNorm, FP4 quantisation and the cache write feed one another and
+// are fused) and section "DSpark adaptation and optimization" (verify positions are
+// contiguous: a row pools with the previous row, only a request's first row reads the
+// ring buffer; the same fused write serves main KV and index K).
+//
+// One wave per row builds both records of the entry the row completes (lane l holds
+// main dims 8l..8l+7 and index dims 2l, 2l+1, so a 16-dim main block spans two lanes
+// and a 32-dim index block sixteen); a second launch recomputes the summaries of the
+// blocks that received entries and moves the ring slots, after every row has read them.
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+// E2M1 code of v = y / 2^e (|v| < 8): the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with
+// ties to the even code, above 5 saturating to 6; sign in bit 3 (none for zero).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | ((v < 0.f && m) ? 8u : 0u);
+}
+
+// OCP MX shared exponent for FP4: floor(log2(amax)) - 2 (E2M1's largest exponent),
+// clamped to E8M0's range; -127 for an all-zero block.
+__device__ __forceinline__ int fp4_scale_exp(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Value of an E2M1 code: exponent bits e = (c >> 1) & 3, mantissa bit c & 1;
+// e = 0 is subnormal (0 or 0.5), otherwise 2^(e-1) * (1 + mantissa / 2).
+__device__ __forceinline__ double e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const double v = e == 0u ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+  return (c & 8u) ? -v : v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// bf16 bits of a double, one round to nearest even (normal bf16 range; outside it the
+// value goes through fp32).
+__device__ __forceinline__ uint32_t bf16_rne_from_double(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  const uint32_t sign = (uint32_t)(u >> 63) << 15;
+  const int exp = (int)((u >> 52) & 0x7FF);
+  const int eb = exp - 1023 + 127;
+  if (d == 0.0) return sign;
+  if (exp == 0 || exp == 0x7FF || eb < 1 || eb > 254) return bf16_bits_rne((float)d);
+  const uint64_t mant = (u & ((1ull << 52) - 1)) | (1ull << 52);             // 53 bits
+  uint64_t r = (mant + ((1ull << 44) - 1) + ((mant >> 45) & 1)) >> 45;        // 8 bits, RNE
+  int e2 = eb;
+  if (r == 256) {
+    r = 128;
+    ++e2;
+  }
+  if (e2 > 254) return bf16_bits_rne((float)d);
+  return sign | ((uint32_t)e2 << 7) | (uint32_t)(r & 0x7F);
+}
+
+struct WriteArgs {
+  RaggedDev g;
+  const int64_t* row_pos;
+  const uint16_t* kv_tok;
+  const uint16_t* idx_tok;
+  uint16_t* ring_kv;
+  uint16_t* ring_idx;
+  const float* gamma_kv;
+  const float* gamma_idx;
+  float eps;
+  uint8_t* main_kv;
+  uint8_t* idx_k;
+  uint16_t* blk_sum;
+};
+
+// Entry completed by row r (-1 if none): t = (P-1)/2 for an odd position P with t < N_b.
+__device__ __forceinline__ int64_t row_entry(const WriteArgs& a, int r, int b, int64_t n) {
+  const int64_t p = a.row_pos[r];
+  if (p < 0 || (p & 1) == 0) return -1;
+  const int64_t t = (p - 1) / 2;
+  return t < n ? t : -1;
+}
+
+__global__ __launch_bounds__(256) void k_write_entries(WriteArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= a.g.R) return;
+  const int b = row_request(a.g, r);
+  int64_t e0, n;
+  req_entries(a.g, b, e0, n);
+  const int64_t t = row_entry(a, r, b, n);
+  if (t < 0) return;
+  int r0, r1;
+  req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
+  const int64_t p = a.row_pos[r];
+  const bool prev_row = r - 1 >= r0 && a.row_pos[r - 1] == p - 1;
+  const uint16_t* pk = prev_row ? a.kv_tok + (int64_t)(r - 1) * CSA2_D : a.ring_kv + (int64_t)b * CSA2_D;
+  const uint16_t* pi = prev_row ? a.idx_tok + (int64_t)(r - 1) * CSA2_IDX_D : a.ring_idx + (int64_t)b * CSA2_IDX_D;
+  const uint16_t* xk = a.kv_tok + (int64_t)r * CSA2_D;
+  const uint16_t* xi = a.idx_tok + (int64_t)r * CSA2_IDX_D;
+  const int64_t row = entry_row(a.g, b, e0, t);
+
+  // Main vector: dims 8 lane .. 8 lane + 7.
+  {
+    const u32x4_t va = load16(pk + 8 * lane), vb = load16(xk + 8 * lane);
+    float y[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = (bf16_lo(va[q]) + bf16_lo(vb[q])) * 0.5f;
+      y[2 * q + 1] = (bf16_hi(va[q]) + bf16_hi(vb[q])) * 0.5f;
+      ss = fmaf(y[2 * q], y[2 * q], ss);
+      ss = fmaf(y[2 * q + 1], y[2 * q + 1], ss);
+    }
+    const float rs = 1.f / sqrtf(wave_sum_f(ss) / (float)CSA2_D + a.eps);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      y[i] = y[i] * rs * a.gamma_kv[8 * lane + i];
+      amax = fmaxf(amax, fabsf(y[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));   // 16-dim block = lanes 2k, 2k+1
+    const int e = fp4_scale_exp(amax);
+    uint32_t codes = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes |= e2m1_code(__builtin_ldexpf(y[i], -e)) << (4 * i);
+    uint8_t* rec = a.main_kv + row * CSA2_MAIN_BYTES;
+    *reinterpret_cast<uint32_t*>(rec + 4 * lane) = codes;
+    if ((lane & 1) == 0) rec[256 + lane / 2] = (uint8_t)(e + 127);
+  }
+  // Index vector: dims 2 lane, 2 lane + 1.
+  {
+    const uint32_t wa = *reinterpret_cast<const uint32_t*>(pi + 2 * lane);
+    const uint32_t wb = *reinterpret_cast<const uint32_t*>(xi + 2 * lane);
+    float y0 = (bf16_lo(wa) + bf16_lo(wb)) * 0.5f, y1 = (bf16_hi(wa) + bf16_hi(wb)) * 0.5f;
+    const float ss = fmaf(y1, y1, y0 * y0);
+    const float rs = 1.f / sqrtf(wave_sum_f(ss) / (float)CSA2_IDX_D + a.eps);
+    y0 = y0 * rs * a.gamma_idx[2 * lane];
+    y1 = y1 * rs * a.gamma_idx[2 * lane + 1];
+    float amax = fmaxf(fabsf(y0), fabsf(y1));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));   // 32-dim block = 16 lanes
+    const int e = fp4_scale_exp(amax);
+    const uint32_t c = e2m1_code(__builtin_ldexpf(y0, -e)) | (e2m1_code(__builtin_ldexpf(y1, -e)) << 4);
+    uint8_t* rec = a.idx_k + row * CSA2_IDX_BYTES;
+    rec[lane] = (uint8_t)c;
+    if ((lane & 15) == 0) rec[64 + lane / 16] = (uint8_t)(e + 127);
+  }
+}
+
+// Summaries of the (at most two) blocks request b's rows wrote into, then its ring slot.
+// Lane l sums index dims 2l, 2l+1 over the block's entries.
+__global__ __launch_bounds__(64) void k_write_summaries(WriteArgs a) {
+  const int b = blockIdx.x, which = blockIdx.y;
+  const int lane = threadIdx.x;
+  int r0, r1;
+  req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
+  if (r1 <= r0) return;
+  int64_t e0, n, bl0, nb;
+  req_entries(a.g, b, e0, n);
+  req_blocks(a.g, b, n, bl0, nb);
+  int64_t tmin = -1, tmax = -1;
+  for (int r = r0; r < r1; ++r) {
+    const int64_t t = row_entry(a, r, b, n);
+    if (t >= 0) {
+      tmin = tmin < 0 ? t : (t < tmin ? t : tmin);
+      tmax = t > tmax ? t : tmax;
+    }
+  }
+  if (tmin >= 0) {
+    const int64_t j = tmin / CSA2_BLOCK + which;
+    if (j <= tmax / CSA2_BLOCK && j < nb) {
+      const int cnt = (int)min<int64_t>(CSA2_BLOCK, n - j * CSA2_BLOCK);
+      double s0 = 0.0, s1 = 0.0;
+      for (int e = 0; e < cnt; ++e) {
+        const uint8_t* rec = a.idx_k + entry_row(a.g, b, e0, j * CSA2_BLOCK + e) * CSA2_IDX_BYTES;
+        const uint32_t c = rec[lane];
+        const uint32_t sb = rec[64 + lane / 16];
+        // E2M1 value of each nibble times the E8M0 scale (exact in double).
+        const double sc = ldexp(1.0, (int)sb - 127);
+        s0 += e2m1_value(c & 15u) * sc;
+        s1 += e2m1_value(c >> 4) * sc;
+      }
+      const uint32_t w = bf16_rne_from_double(s0 / cnt) | (bf16_rne_from_double(s1 / cnt) << 16);
+      *reinterpret_cast<uint32_t*>(a.blk_sum + block_row(a.g, b, bl0, j) * CSA2_IDX_D + 2 * lane) = w;
+    }
+  }
+  // Ring slot: the last row's token when it waits for its partner (even position).
+  if (which == 0) {
+    const int64_t p = a.row_pos[r1 - 1];
+    if (p >= 0 && (p & 1) == 0) {
+      const uint16_t* xk = a.kv_tok + (int64_t)(r1 - 1) * CSA2_D;
+      const uint16_t* xi = a.idx_tok + (int64_t)(r1 - 1) * CSA2_IDX_D;
+      *reinterpret_cast<u32x4_t*>(a.ring_kv + (int64_t)b * CSA2_D + 8 * lane) = load16(xk + 8 * lane);
+      *reinterpret_cast<uint32_t*>(a.ring_idx + (int64_t)b * CSA2_IDX_D + 2 * lane) =
+          *reinterpret_cast<const uint32_t*>(xi + 2 * lane);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const RaggedDev& g, const int64_t* row_pos, const uint16_t* kv_tok,
+                              const uint16_t* idx_tok, uint16_t* ring_kv, uint16_t* ring_idx, const float* gamma_kv,
+                              const float* gamma_idx, float eps, uint8_t* main_kv, uint8_t* idx_k, uint16_t* blk_sum,
+                              hipStream_t st) {
+  if (g.R == 0 || g.B == 0) return hipSuccess;
+  WriteArgs a{g, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, eps, main_kv, idx_k, blk_sum};
+  k_write_entries<<<dim3((g.R + 3) / 4), dim3(256), 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_write_summaries<<<dim3(g.B, 2), dim3(64), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -5,6 +5,7 @@ from .generator import (  # noqa: F401
     Workload,
     make_config,
     make_workload,
+    make_write_inputs,
     to_paged,
     verify_row_len,
 )

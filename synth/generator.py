@@ -31,7 +31,8 @@ request ``b`` of a config does not depend on how many requests follow it:
 * ``(seed, 1, b, 4, c)``        main latents [<=16384, 512] N(0,1) of chunk c;
 * ``(seed, 1, b, 5)``           window tokens [T_b, 512] N(0,1).
 * ``(seed, 2, 1)``              paged copies: the page permutation, then the bytes of
-                                spare pages and of the unused tail rows of last pages.
+                                spare pages and of the unused tail rows of last pages;
+* ``(seed, 3)``                 cache-write inputs: tokens, ring slots, RMSNorm gains.
 
 All draws are float32 (page bytes: uniform uint8 / uint16).
 """
@@ -363,6 +364,30 @@ def to_paged(wl: Workload, seed: int | None = None, spare_pages: int | None = No
     out.idx_k, out.main_kv, out.blk_sum = idx_k, main_kv, blk_sum
     out.page_table, out.total_pages = page_table, P
     return out
+
+
+def make_write_inputs(wl: Workload, seed: int, last_even: bool = True) -> dict:
+    """Inputs of a cache write for the rows of ``wl``: the rows of request b hold
+    consecutive token positions ending at 2 N_b (even: that token waits in the ring slot)
+    or 2 N_b - 1 (odd: it completes entry N_b - 1), so the write fills the request's last
+    entries; tokens, ring slots N(0,1) as bf16; RMSNorm gains U(0.5, 1.5).  Random stream
+    ``(seed, 3)``."""
+    rng = _rng(seed, 3)
+    R, B = wl.num_rows, wl.num_requests
+    pos = np.zeros(R, dtype=np.int64)
+    for b in range(B):
+        r0, r1 = int(wl.row_off[b]), int(wl.row_off[b + 1])
+        last = 2 * wl.n_entries(b) if last_even else 2 * wl.n_entries(b) - 1
+        pos[r0:r1] = last - (r1 - r0) + 1 + np.arange(r1 - r0)
+    return dict(
+        row_pos=pos,
+        kv_tok=bf16_bits_from_f32(rng.standard_normal((R, D_LATENT), dtype=np.float32)),
+        idx_tok=bf16_bits_from_f32(rng.standard_normal((R, D_IDX), dtype=np.float32)),
+        ring_kv=bf16_bits_from_f32(rng.standard_normal((B, D_LATENT), dtype=np.float32)),
+        ring_idx=bf16_bits_from_f32(rng.standard_normal((B, D_IDX), dtype=np.float32)),
+        gamma_kv=rng.uniform(0.5, 1.5, D_LATENT).astype(np.float32),
+        gamma_idx=rng.uniform(0.5, 1.5, D_IDX).astype(np.float32),
+    )
 
 
 def verify_row_len(wl: Workload) -> np.ndarray:

@@ -459,3 +459,94 @@ def test_mx_attention_closed_forms_and_bound():
     assert np.allclose(l1, l0, rtol=0, atol=1e-12)
     assert np.all(np.abs(o1 - o0) <= bound / 2 + 1e-12)
     assert np.abs(o1 - o0).max() > 0        # P really is rounded
+
+
+# ---------------------------------------------------------------------------------
+# Cache write.
+# ---------------------------------------------------------------------------------
+
+def test_fp4_encode_matches_the_input_generators_encoder():
+    # Two independent encoders of the same OCP MX rule (the generator's uses threshold
+    # counts, the oracle's nearest-value search).
+    from synth.generator import encode_fp4_blocks
+    rng = np.random.default_rng(40)
+    x = (rng.standard_normal((200, 512)) * np.exp(rng.uniform(-20, 20, size=(200, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[1, :16] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, 0.0, 4.5, 5.5, 1e-30, -1.0, 0.1]
+    x[2, :32] = np.ldexp(np.arange(32) / 4.0, -3)          # every E2M1 midpoint at scale 2^-3
+    for block in (16, 32):
+        got = oracle.pack_fp4_record(*oracle.fp4_encode(x, block))
+        assert np.array_equal(got, encode_fp4_blocks(x, block)), block
+    # Round trip: values on the grid come back unchanged.
+    codes, exps = oracle.fp4_encode(x, 16)
+    rec = oracle.pack_fp4_record(codes, exps)
+    back = oracle.dequant_fp4_records(rec, 512, 16)
+    again = oracle.pack_fp4_record(*oracle.fp4_encode(back, 16))
+    assert np.array_equal(again, rec)
+
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal(5000).astype(np.float32).astype(np.float64)   # fp32-exact inputs
+    x[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.0]
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_rne(x), ref)
+
+
+def _write_case(seed, lens, rows, last_even=True):
+    from synth import make_workload, make_write_inputs
+    wl = make_workload("w", seed, lens, rows_per_req=rows, n_needles=2)
+    w = make_write_inputs(wl, seed + 1, last_even)
+    return (wl, w["row_pos"], w["kv_tok"], w["idx_tok"], w["ring_kv"], w["ring_idx"], w["gamma_kv"],
+            w["gamma_idx"])
+
+
+def test_cache_write_rules():
+    wl, pos, kv, ik, rkv, ridx, gk, gi = _write_case(42, [300, 64 * 5], [5, 6])
+    res = oracle.cache_write(wl, pos, kv, ik, rkv, ridx, gk, gi)
+    # Entries written: odd positions only, below N_b.
+    assert sorted(res["written"]) == sorted((b, (int(p) - 1) // 2) for r, p in enumerate(pos) if p % 2 == 1
+                                            for b in [int(wl.row_req[r])] if (int(p) - 1) // 2 < wl.n_entries(b))
+    # Rows not written are untouched.
+    changed = np.flatnonzero((res["idx_k"] != wl.idx_k).any(axis=1) | (res["main_kv"] != wl.main_kv).any(axis=1))
+    rows = {int(oracle.entry_rows(wl, b, np.array([t]))[0]) for (b, t) in res["written"]}
+    assert set(changed.tolist()) <= rows
+    # The pooling partner of a request's first row (here request 1: 6 rows ending at
+    # 2 N_b start at an odd position) is its ring slot; the same token as an extra row
+    # just before it gives the same records.
+    b = 1
+    r0 = int(wl.row_off[b])
+    assert pos[r0] % 2 == 1
+    kv2 = np.concatenate([kv[:r0], rkv[b:b + 1], kv[r0:]])
+    ik2 = np.concatenate([ik[:r0], ridx[b:b + 1], ik[r0:]])
+    wl2 = type(wl)(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+    wl2.row_off = wl.row_off + np.array([0, 0, 1], dtype=np.int32)
+    wl2.row_req = np.concatenate([wl.row_req[:r0], [b], wl.row_req[r0:]]).astype(np.int32)
+    pos2 = np.concatenate([pos[:r0], [pos[r0] - 1], pos[r0:]])
+    kv2_ring, ik2_ring = rkv.copy(), ridx.copy()
+    kv2_ring[b] = 0
+    ik2_ring[b] = 0
+    res2 = oracle.cache_write(wl2, pos2, kv2, ik2, kv2_ring, ik2_ring, gk, gi)
+    assert np.array_equal(res2["main_kv"], res["main_kv"]) and np.array_equal(res2["idx_k"], res["idx_k"])
+    # Summaries: bf16 of the mean of the block's dequantised keys.
+    t = max(t for (bb, t) in res["written"] if bb == 1)
+    j = t // 64
+    keys = oracle.dequant_idx(res["idx_k"][oracle.entry_rows(wl, 1, np.arange(64 * j, min(64 * j + 64, 320)))])
+    assert np.array_equal(res["blk_sum"][int(wl.block_off[1]) + j], oracle.bf16_rne(keys.mean(axis=0)))
+    # The last row of request 1 (position 2 N_b, even) went to its ring slot.
+    assert np.array_equal(res["ring_kv"][1], kv[int(wl.row_off[2]) - 1])
+
+
+def test_cache_write_is_scale_invariant():
+    # RMSNorm: scaling both pooled tokens by a power of two leaves every record alone.
+    wl, pos, kv, ik, rkv, ridx, gk, gi = _write_case(43, [200], [4])
+    a = oracle.cache_write(wl, pos, kv, ik, rkv, ridx, gk, gi, eps=1e-30)
+    up = lambda bits: (bits.astype(np.uint32) + (3 << 7)).astype(np.uint16)   # x 8 in bf16 (exponent + 3)
+    b = oracle.cache_write(wl, pos, up(kv), up(ik), up(rkv), up(ridx), gk, gi, eps=1e-30)
+    assert np.array_equal(a["main_kv"], b["main_kv"]) and np.array_equal(a["idx_k"], b["idx_k"])
+    # Doubling gamma doubles every value: same codes, every scale byte one higher.
+    c = oracle.cache_write(wl, pos, kv, ik, rkv, ridx, gk * 2, gi * 2, eps=1e-30)
+    for (bb, t) in a["written"]:
+        row = int(oracle.entry_rows(wl, bb, np.array([t]))[0])
+        assert np.array_equal(c["main_kv"][row, :256], a["main_kv"][row, :256])
+        assert np.array_equal(c["main_kv"][row, 256:].astype(int), a["main_kv"][row, 256:].astype(int) + 1)
