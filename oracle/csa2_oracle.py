@@ -52,6 +52,13 @@ and translates positions into KV page addresses.  Read here as:
 [KT] contrasts full-BF16 sparse MLA with a route that rounds Q and P to MXFP8 (OCP MX:
 E4M3 elements, one E8M0 scale per 32 values); joint_attention_mx states that route.
 
+[SGL] "Small-operator fusion and GEMV" and "DSpark adaptation and optimization" name the
+fused cache-write chain (pair pooling, RMSNorm, FP4 quantisation, cache write, reused for
+index K; verify rows pool with the previous row, the first row with a ring buffer) but
+not its arithmetic; cache_write takes the plainest reading: the mean of the two tokens,
+x * gamma / sqrt(mean(x^2) + eps), OCP MX FP4, and block summaries as the bf16 mean of the
+block's dequantised index keys.
+
 Every function here is pinned by tests in tests/test_formats.py and tests/test_oracle.py
 (format tables against a library decoder and the OCP MX value table, brute-force exact
 rational scores, brute-force selection, the dense-attention special case, LSE merging
