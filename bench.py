@@ -45,6 +45,7 @@ def _hip():
     lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -427,7 +428,6 @@ def main() -> int:
         build()
     torch.cuda.set_device(0)
     hip = _hip()
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     if args.profile_scale:
         roof, aroof = scale_rooflines(csa2, hip, steps=20)

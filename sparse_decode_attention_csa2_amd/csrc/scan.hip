@@ -25,7 +25,15 @@ constexpr int kRsrcWord3 = 0x00020000;             // raw buffer descriptor, gfx
 #ifndef CSA2_SCAN_DEPTH
 #define CSA2_SCAN_DEPTH 3
 #endif
-constexpr int kMaxIters = 8;                        // chunks per wave, at most
+// Chunks per wave, at most: 4 (workgroups of 1,024 entries) measured fastest on the
+// 64 x 65,536-entry scan (56-57 us against 58-59 us at 8, 59 at 16, 63-64 at 1).
+#ifndef CSA2_SCAN_MAX_ITERS
+#define CSA2_SCAN_MAX_ITERS 4
+#endif
+#ifndef CSA2_SCAN_WG_STAGE
+#define CSA2_SCAN_WG_STAGE 1
+#endif
+constexpr int kMaxIters = CSA2_SCAN_MAX_ITERS;      // chunks per wave, at most
 constexpr int kWgRows = 4;                          // rows staged per workgroup
 #ifndef CSA2_SCAN_WAVES_PER_EU
 #define CSA2_SCAN_WAVES_PER_EU 4
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     // Scores are staged in LDS: with at most kWgRows rows the whole workgroup's scores
     // stay until the end and leave as contiguous row segments (one write burst per
     // workgroup); with more rows each wave flushes every chunk.
-    constexpr bool kWgStage = 2 * MAXPAIRS <= kWgRows;
+    constexpr bool kWgStage = CSA2_SCAN_WG_STAGE && 2 * MAXPAIRS <= kWgRows;
     constexpr int kStageRows = kWgStage ? 2 * MAXPAIRS : 1;
     constexpr int kStageLen = kWgStage ? kWaves * 64 * kMaxIters : 1;
     __shared__ __align__(16) float wstage[kStageRows][kStageLen];
