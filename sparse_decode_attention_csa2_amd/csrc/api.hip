@@ -415,7 +415,10 @@ static size_t decode_layout(const csa2_decode_args* a, char* base, float** score
   if (sel) *sel = a->sel_idx ? a->sel_idx : sl;
   int32_t* ns = a->n_sel ? nullptr : c.take<int32_t>((size_t)R);
   if (n_sel) *n_sel = a->n_sel ? a->n_sel : ns;
-  int32_t* sr = rg.page_table ? c.take<int32_t>((size_t)R * a->k) : nullptr;
+  // Pool rows of the picks (int32): written by the fine top-k so that attention reads
+  // records without first looking up its request's offsets.
+  const bool rows = rg.page_table || rg.total_entries < (int64_t(1) << 31);
+  int32_t* sr = rows ? c.take<int32_t>((size_t)R * a->k) : nullptr;
   if (sel_rows) *sel_rows = sr;
   const size_t ab = attn_workspace_bytes(R, a->k);
   char* aw = c.take<char>(ab);
@@ -463,8 +466,8 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   const int64_t ld = a->scores ? a->scores_ld : (int64_t)round_up((size_t)(g.max_entries > 0 ? g.max_entries : 1), 64);
   const int64_t blk_ld = (int64_t)round_up((size_t)(blocks_of(g.max_entries) > 0 ? blocks_of(g.max_entries) : 1), 64);
 
-  // Paged pools: the fine top-k also writes the picks' pool rows (translation fused into
-  // the selection), and attention reads those.
+  // The fine top-k also writes the picks' pool rows (for paged pools the page
+  // translation is fused into the selection), and attention reads those.
   AttnArgs at{};
   CHECK(attn_args(g, a->q, a->main_kv, sel_rows ? sel_rows : sel, n_sel, a->k, a->swa, a->swa_scale, a->sm_scale,
                   a->out, a->lse, attn_ws, attn_bytes, at));

@@ -42,28 +42,34 @@ struct RowKeys {
   int n_swa;
 };
 
+// ROWS: the selection holds pool rows (a.sel_rows != 0), so the request's offsets are
+// not needed and not loaded.
+template <bool ROWS = false>
 __device__ __forceinline__ RowKeys row_keys(const AttnArgs& a, int r) {
   RowKeys k;
-  const int64_t vis = row_len_raw(a.g, r);
-  const int b = row_request(a.g, r);
-  int64_t e0, n;
-  req_entries(a.g, b, e0, n);
-  n = row_visible(a.g, vis, n);
-  k.e0 = a.sel_rows ? 0 : e0;
-  k.n = a.sel_rows ? a.g.total_entries : n;
-  int ns = a.n_sel[r];
-  k.n_main = ns < 0 ? 0 : (ns > a.sel_ld ? a.sel_ld : ns);
-  int64_t s0 = a.g.row_swa_start[r];
-  int len = a.g.row_swa_len[r];
-  len = len < 0 ? 0 : (len > CSA2_SWA_MAX ? CSA2_SWA_MAX : len);
-  if (s0 < 0 || s0 >= a.g.swa_tokens) {
-    s0 = 0;
-    len = 0;
-  } else if (s0 + len > a.g.swa_tokens) {
-    len = (int)(a.g.swa_tokens - s0);
+  if (ROWS) {
+    k.e0 = 0;
+    k.n = a.g.total_entries;
+  } else {
+    const int64_t vis = row_len_raw(a.g, r);
+    const int b = row_request(a.g, r);
+    int64_t e0, n;
+    req_entries(a.g, b, e0, n);
+    n = row_visible(a.g, vis, n);
+    k.e0 = a.sel_rows ? 0 : e0;
+    k.n = a.sel_rows ? a.g.total_entries : n;
   }
-  k.s0 = s0;
-  k.n_swa = len;
+  // All loads first, then selects (a branch here would let the compiler sink a load
+  // into it, behind the others).
+  const int ns = a.n_sel[r];
+  const int64_t s0 = a.g.row_swa_start[r];
+  int len = a.g.row_swa_len[r];
+  k.n_main = ns < 0 ? 0 : (ns > a.sel_ld ? a.sel_ld : ns);
+  len = len < 0 ? 0 : (len > CSA2_SWA_MAX ? CSA2_SWA_MAX : len);
+  const bool bad = s0 < 0 || s0 >= a.g.swa_tokens;
+  const int64_t room = a.g.swa_tokens - s0;
+  k.s0 = bad ? 0 : s0;
+  k.n_swa = bad ? 0 : (int)(len < room ? len : room);
   return k;
 }
 
@@ -118,7 +124,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 // reads its A operand (V^T) from the same key-major copy with transposing LDS loads.
 // MX: the MXFP8 route (Q and P rounded to MXFP8 before their products); otherwise Q as
 // given and P as exact-to-2^-17 bf16 hi + lo parts.
-template <bool MX>
+template <bool MX, bool ROWS>
 __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   constexpr int TK = kAttnTileKeys;   // 64
   constexpr int KB = TK / 32;         // 32-key groups
@@ -129,11 +135,39 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   __shared__ int kval[TK];
 
   const int r = blockIdx.y, split = blockIdx.x;
-  const RowKeys rk = row_keys(a, r);
-  const int n_keys = rk.n_main + rk.n_swa;
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), hg = wave & 3, dh = wave >> 2;
   const int h = hg * 16 + ln;
+  const int k_begin = split * a.tiles_per_split * TK;
+
+  // Dequant role: keys 32u + 2kp + e (e < 2) of a tile, dims 32ch .. 32ch+31.  A tile's
+  // keys are fetched in two steps that every thread takes without branching (so no load
+  // waits on another path's registers): the selected positions (sel_pos), then the
+  // records (load_keys), each address clamped to valid memory and the key's kind
+  // deciding afterwards what the loaded bytes mean.  Positions are read clamped to the
+  // row's sel_ld slots rather than its count, so the first tile's positions load
+  // alongside the row's counts.
+  const int kp = tid & 15, ch = (tid >> 4) & 15, u = tid >> 8;
+  const int32_t* sel_row = a.sel + (int64_t)r * a.sel_ld;
+  int32_t pos_raw[2];
+  auto sel_pos = [&](int kt) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) pos_raw[e] = sel_row[min(kt + 32 * u + 2 * kp + e, a.sel_ld - 1)];
+  };
+  sel_pos(k_begin);
+  // Query fragments of this wave's dims (B operand of S^T = K Q^T): lane holds
+  // q[h][256dh + 32st + 8g + j].  Loaded before anything that depends on the row.
+  bf16x8_t qb[8];
+  {
+    const uint16_t* qp = a.q + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 256 * dh + 8 * g;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
+  }
+  // Keep these loads ahead of the row checks below (the compiler would otherwise sink
+  // them past the early exits, behind the counts they do not depend on).
+  asm volatile("" ::: "memory");
+  const RowKeys rk = row_keys<ROWS>(a, r);
+  const int n_keys = rk.n_main + rk.n_swa;
 
   if (n_keys == 0) {
     if (split == 0) {
@@ -142,7 +176,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     }
     return;
   }
-  const int k_begin = split * a.tiles_per_split * TK;
   if (k_begin >= n_keys) return;
   const int k_end = min(n_keys, k_begin + a.tiles_per_split * TK);
 
@@ -151,19 +184,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   for (int t = 0; t < 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Dequant role: keys 32u + 2kp + e (e < 2) of a tile, dims 32ch .. 32ch+31.  A tile's
-  // keys are fetched in two steps that every thread takes without branching (so no load
-  // waits on another path's registers): the selected positions (sel_pos), then the
-  // records (load_keys), each address clamped to valid memory and the key's kind
-  // deciding afterwards what the loaded bytes mean.
-  const int kp = tid & 15, ch = (tid >> 4) & 15, u = tid >> 8;
-  const int32_t* sel_row = a.sel + (int64_t)r * a.sel_ld;
-  const int last_main = rk.n_main > 0 ? rk.n_main - 1 : 0;
-  int32_t pos_raw[2];
-  auto sel_pos = [&](int kt) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) pos_raw[e] = sel_row[min(kt + 32 * u + 2 * kp + e, last_main)];
-  };
   const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.q);   // any readable 16-B aligned bytes
   KeyRegs kr[2];
   auto load_keys = [&](int kt) {
@@ -190,15 +210,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
       kr[e] = k;
     }
   };
-  sel_pos(k_begin);
-  // Query fragments of this wave's dims (B operand of S^T = K Q^T): lane holds
-  // q[h][256dh + 32st + 8g + j].
-  bf16x8_t qb[8];
-  {
-    const uint16_t* qp = a.q + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 256 * dh + 8 * g;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qb[st] = as_bf16x8(load16(qp + 32 * st));
-  }
   load_keys(k_begin);
   if constexpr (MX) {
     // MXFP8 route: block st of 32 dims = this lane's 8 values and those of lanes xor 16
@@ -390,8 +401,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   constexpr int kBatch = 8;
   f32x4_t v[kBatch];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u)
-    v[u] = u < ns ? *reinterpret_cast<const f32x4_t*>(src + u * kStride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < kBatch; ++u)   // every launched split has a partial slot; only u < ns are used
+    v[u] = u < a.splits ? *reinterpret_cast<const f32x4_t*>(src + u * kStride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, msh[s][ln]);
@@ -447,10 +458,18 @@ size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
 
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  if (a.qp_route == CSA2_QP_MXFP8)
-    k_attn<true><<<dim3(a.splits, a.g.R), dim3(512), 0, st>>>(a);
-  else
-    k_attn<false><<<dim3(a.splits, a.g.R), dim3(512), 0, st>>>(a);
+  const dim3 grid(a.splits, a.g.R);
+  if (a.qp_route == CSA2_QP_MXFP8) {
+    if (a.sel_rows)
+      k_attn<true, true><<<grid, dim3(512), 0, st>>>(a);
+    else
+      k_attn<true, false><<<grid, dim3(512), 0, st>>>(a);
+  } else {
+    if (a.sel_rows)
+      k_attn<false, true><<<grid, dim3(512), 0, st>>>(a);
+    else
+      k_attn<false, false><<<grid, dim3(512), 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -283,17 +283,10 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // flight per thread; kbuf is zero-padded to whole chunks.  Publishes the per-wave key
 // range and zeroes the first histogram buffer; the caller then needs one barrier.
 template <class ValidF, class LoadF>
-__device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShared& sh) {
+__device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShared& sh,
+                       const float* pre = nullptr) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, cnt = 0u;
-  for (int base = 0; base < n; base += NT * kGB) {
-    float v[kGB];
-    bool ok[kGB];
-#pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int i = base + u * NT + (int)threadIdx.x;
-      ok[u] = (i < n) & valid(i);   // valid() must accept any i (clamped reads)
-      v[u] = load(i, ok[u]);
-    }
+  auto keys = [&](int base, const float (&v)[kGB], const bool (&ok)[kGB]) {
 #pragma unroll
     for (int u = 0; u < kGB; ++u) {
       const int i = base + u * NT + (int)threadIdx.x;
@@ -304,6 +297,30 @@ __device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShare
       hi = max(hi, kk);
       cnt += kk ? 1u : 0u;
     }
+  };
+  int base0 = 0;
+  if (pre) {   // the first batch was loaded by the caller
+    float v[kGB];
+    bool ok[kGB];
+#pragma unroll
+    for (int u = 0; u < kGB; ++u) {
+      const int i = u * NT + (int)threadIdx.x;
+      ok[u] = (i < n) & valid(i);
+      v[u] = pre[u];
+    }
+    keys(0, v, ok);
+    base0 = NT * kGB;
+  }
+  for (int base = base0; base < n; base += NT * kGB) {
+    float v[kGB];
+    bool ok[kGB];
+#pragma unroll
+    for (int u = 0; u < kGB; ++u) {
+      const int i = base + u * NT + (int)threadIdx.x;
+      ok[u] = (i < n) & valid(i);   // valid() must accept any i (clamped reads)
+      v[u] = load(i, ok[u]);
+    }
+    keys(base, v, ok);
   }
   const int padded = (n + kWave - 1) / kWave * kWave;
   for (int i = n + (int)threadIdx.x; i < padded; i += NT) kbuf[i] = 0u;
@@ -312,19 +329,32 @@ __device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShare
 }
 
 template <bool PAGED>
-__device__ __forceinline__ int row_blocks(const SelectArgs& a, int r, int64_t& n) {
+__device__ __forceinline__ int row_blocks(const SelectArgs& a, int r, int64_t& n, int64_t& e0) {
   const int64_t vis = row_len_raw(a.g, r);
   const int b = row_request(a.g, r);
-  int64_t e0, bl0, nb;
+  int64_t bl0, nb;
   req_entries(a.g, b, e0, n, PAGED);
   n = row_visible(a.g, vis, n);
   req_blocks(a.g, b, n, bl0, nb, PAGED);
   return (int)nb;
 }
 
+// First gather batch of row r's block scores, loaded before the row's offsets are known
+// (the loads are clamped to the row's blk_ld <= kLdsBlocks slots).
+__device__ __forceinline__ void prefetch_blocks(const SelectArgs& a, int r, float (&pre)[kGB]) {
+  const float* bs = a.blk_scores + (int64_t)r * a.blk_ld;
+  const int lim = (int)a.blk_ld - 1;
+#pragma unroll
+  for (int u = 0; u < kGB; ++u) pre[u] = bs[min(u * NT + (int)threadIdx.x, lim)];
+  // Keep the loads here, ahead of the offset loads' waits.
+  asm volatile("" ::: "memory");
+}
+
 // Coarse stage of row r: kept blocks (ascending) into sh.kl / sh.nk and, if given, the
-// global kept list.
-__device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32_t* kbuf) {
+// global kept list.  BIG: blk_ld may exceed kLdsBlocks (rows with more blocks rank
+// straight from global memory); otherwise pre holds the first gather batch.
+template <bool BIG>
+__device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32_t* kbuf, const float* pre) {
   const float* bs = a.blk_scores + (int64_t)r * a.blk_ld;
   int32_t* kout = a.kept ? a.kept + (int64_t)r * a.kept_ld : nullptr;
   if (threadIdx.x == 0) sh.flag = 0;
@@ -334,8 +364,13 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
     if (i == nb - 1) sh.flag = 1;
   };
   int cnt;
-  if (nb <= kLdsBlocks) {
-    gather(nb, [](int) { return true; }, [&](int i, bool ok) { return bs[ok ? i : 0]; }, kbuf, sh);
+  if (!BIG || nb <= kLdsBlocks) {
+    // The gather runs over the row's blk_ld slots (a launch constant, >= nb) with its
+    // loads clamped to them, so they need not wait for the request's offsets; items at
+    // or past nb are masked to empty keys.
+    const int lim = (int)(a.blk_ld < kLdsBlocks ? a.blk_ld : kLdsBlocks);
+    gather(lim, [&](int i) { return i < nb; }, [&](int i, bool) { return bs[min(i, lim - 1)]; }, kbuf, sh,
+           BIG ? nullptr : pre);
     __syncthreads();
     cnt = sel_top([&](int i) { return kbuf[i]; }, nb, valid_count(sh), a.n_keep, sh, emit);
   } else {
@@ -374,11 +409,11 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
 
 // Fine stage of row r over the kept blocks sh.kl[0 .. nk) (chunk s = kept block s,
 // lane = entry) or, with all_entries, over entries 0 .. n-1.  Candidates are the items
-// with a key: positions the row sees whose score is not NaN.
-// PAGED: paged pools; the picks' pool rows then also go to a.sel_rows when it is set
-// (contiguous pools get an instantiation without that code).
+// with a key: positions the row sees whose score is not NaN.  When a.sel_rows is set
+// the picks' pool rows go there too: e0 + position for contiguous pools, the page
+// table's row for paged ones (PAGED).
 template <bool PAGED>
-__device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_entries, SelShared& sh,
+__device__ void fine(const SelectArgs& a, int r, int64_t n, int64_t e0, int nk, bool all_entries, SelShared& sh,
                      uint32_t* kbuf) {
   const float* sc = a.scores + (int64_t)r * a.ld;
   const int k = a.k;
@@ -390,7 +425,7 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_ent
   // kept block s (nk <= 129 < NT) once, with its load in flight together with the
   // gather's, and the emit below translates from LDS.
   static_assert(CSA2_KEEP_MAX + 1 <= NT, "one kept block per thread");
-  int32_t* rows = (PAGED && a.sel_rows && !all_entries) ? a.sel_rows + (int64_t)r * k : nullptr;
+  int32_t* rows = (a.sel_rows && !all_entries) ? a.sel_rows + (int64_t)r * k : nullptr;
   int32_t kpage = 0;
   if (PAGED && rows && (int)threadIdx.x < nk) {
     const int64_t kb = sh.kl[threadIdx.x];
@@ -420,23 +455,25 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int nk, bool all_ent
   const int take = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), k, sh, [&](int pos, int i) {
     sel[pos] = all_entries ? i : (int32_t)pos_of(i);
     if (ss) ss[pos] = key_score(kbuf[i]);
-    if (PAGED && rows) rows[pos] = sh.kpage[i / CSA2_BLOCK] + (i % CSA2_BLOCK);
+    if (rows) rows[pos] = PAGED ? sh.kpage[i / CSA2_BLOCK] + (i % CSA2_BLOCK) : (int32_t)(e0 + pos_of(i));
   });
   for (int i = take + threadIdx.x; i < k; i += NT) {
     sel[i] = -1;
     if (ss) ss[i] = 0.f;
-    if (PAGED && rows) rows[i] = -1;
+    if (rows) rows[i] = -1;
   }
   if (threadIdx.x == 0) a.n_sel[r] = take;
 }
 
-template <bool PAGED>
+template <bool PAGED, bool BIG>
 __global__ __launch_bounds__(NT) void k_block_select(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
-  int64_t n;
-  const int nb = row_blocks<PAGED>(a, blockIdx.x, n);
-  coarse(a, blockIdx.x, nb, sh, kbuf);
+  float pre[kGB];
+  if (!BIG) prefetch_blocks(a, blockIdx.x, pre);
+  int64_t n, e0;
+  const int nb = row_blocks<PAGED>(a, blockIdx.x, n, e0);
+  coarse<BIG>(a, blockIdx.x, nb, sh, kbuf, pre);
 }
 
 template <bool PAGED>
@@ -444,8 +481,8 @@ __global__ __launch_bounds__(NT) void k_topk(SelectArgs a, int all_entries) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kMaxCand];
   const int r = blockIdx.x;
-  int64_t n;
-  row_blocks<PAGED>(a, r, n);
+  int64_t n, e0;
+  row_blocks<PAGED>(a, r, n, e0);
   int nk = 0;
   if (!all_entries) {
     nk = a.n_kept[r];
@@ -454,30 +491,35 @@ __global__ __launch_bounds__(NT) void k_topk(SelectArgs a, int all_entries) {
     for (int i = threadIdx.x; i < nk; i += NT) sh.kl[i] = a.kept[(int64_t)r * a.kept_ld + i];
     __syncthreads();
   }
-  fine<PAGED>(a, r, n, nk, all_entries != 0, sh, kbuf);
+  fine<PAGED>(a, r, n, e0, nk, all_entries != 0, sh, kbuf);
 }
 
 // Both stages for one row; the block keys and the candidate keys share one LDS buffer.
-template <bool PAGED>
+template <bool PAGED, bool BIG>
 __global__ __launch_bounds__(NT) void k_select_fused(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
   const int r = blockIdx.x;
-  int64_t n;
-  const int nb = row_blocks<PAGED>(a, r, n);
-  coarse(a, r, nb, sh, kbuf);
+  float pre[kGB];
+  if (!BIG) prefetch_blocks(a, r, pre);
+  int64_t n, e0;
+  const int nb = row_blocks<PAGED>(a, r, n, e0);
+  coarse<BIG>(a, r, nb, sh, kbuf, pre);
   __syncthreads();
-  fine<PAGED>(a, r, n, sh.nk, false, sh, kbuf);
+  fine<PAGED>(a, r, n, e0, sh.nk, false, sh, kbuf);
 }
 
 }  // namespace
 
 hipError_t launch_block_select(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
+  const bool big = a.blk_ld > kLdsBlocks;
   if (a.g.page_table)
-    k_block_select<true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+    big ? k_block_select<true, true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a)
+        : k_block_select<true, false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
   else
-    k_block_select<false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+    big ? k_block_select<false, true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a)
+        : k_block_select<false, false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -492,10 +534,13 @@ hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st) {
 
 hipError_t launch_select_fused(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
+  const bool big = a.blk_ld > kLdsBlocks;
   if (a.g.page_table)
-    k_select_fused<true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+    big ? k_select_fused<true, true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a)
+        : k_select_fused<true, false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
   else
-    k_select_fused<false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+    big ? k_select_fused<false, true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a)
+        : k_select_fused<false, false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
   return hipGetLastError();
 }
 
