@@ -76,16 +76,23 @@ __device__ __forceinline__ RowKeys row_keys(const AttnArgs& a, int r) {
 // One key's raw record slice as loaded by its thread (dims 32ch .. 32ch+31).
 struct KeyRegs {
   u32x4_t c0, c1;     // main: c0 = 16 code bytes; window: c0, c1 = 32 E4M3 bytes
-  uint32_t sc;        // main: two E8M0 bytes (blocks 2ch, 2ch+1); window: fp32 scale bits
+  uint32_t sc;        // as loaded: main: the 4 E8M0 bytes of blocks 4(ch/2) .. 4(ch/2)+3;
+                      // window: fp32 scale bits.  Nothing reads it before convert_key, so
+                      // the loads stay in flight while the previous tile computes.
   int kind;           // 0 empty, 1 main entry, 2 window token
 };
 
-// Exact bf16 values of a key's 32 dims as 16 packed words (element 2q in the low half).
-__device__ __forceinline__ void convert_key(const KeyRegs& k, uint32_t (&w)[16]) {
+// E8M0 scales of a main key's blocks 2ch and 2ch+1 (from the loaded scale word).
+__device__ __forceinline__ uint32_t main_scales(const KeyRegs& k, int ch) { return k.sc >> (16 * (ch & 1)); }
+
+// Exact bf16 values of a key's 32 dims (dims 32ch .. 32ch+31) as 16 packed words
+// (element 2q in the low half).
+__device__ __forceinline__ void convert_key(const KeyRegs& k, int ch, uint32_t (&w)[16]) {
   if (k.kind == 1) {
+    const uint32_t s2 = main_scales(k, ch);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const u32x4_t x = __builtin_bit_cast(u32x4_t, fp4x8_to_bf16(k.c0[d], e8m0_operand((k.sc >> (8 * (d >> 1))) & 255u)));
+      const u32x4_t x = __builtin_bit_cast(u32x4_t, fp4x8_to_bf16(k.c0[d], e8m0_operand((s2 >> (8 * (d >> 1))) & 255u)));
       w[4 * d] = x[0];
       w[4 * d + 1] = x[1];
       w[4 * d + 2] = x[2];
@@ -204,8 +211,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
       KeyRegs k;
       k.c0 = load16(pa);
       k.c1 = load16(pb);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(ps);
-      k.sc = is_main ? (sw >> (16 * (ch & 1))) & 0xFFFFu : sw;
+      k.sc = *reinterpret_cast<const uint32_t*>(ps);
       k.kind = is_main ? 1 : (is_win ? 2 : 0);
       kr[e] = k;
     }
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       uint32_t w[16];
-      convert_key(kr[e], w);
+      convert_key(kr[e], ch, w);
       uint16_t* k0 = Kl + (32 * u + 2 * kp + e) * KLS + 32 * ch;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
