@@ -132,3 +132,18 @@ def test_decode_keep_all_is_dense_attention(csa2):
                                             wl.sm_scale)
             rel, dl = parity.attn_error(got["out"][r], got["lse"][r], ro, rl)
             assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS
+
+
+def test_decode_beyond_lds_block_buffer(csa2):
+    # A request with more 64-entry blocks than the select's LDS key buffer holds (16,384):
+    # its coarse stage ranks straight from global memory, while the shorter request of
+    # the same launch (blk_ld above the buffer too) takes the LDS path without prefetch.
+    lens = [64 * 16384 + 70, 64 * 300 + 5]
+    wl = make_workload("beyond", 23, lens, rows_per_req=[1, 2], n_needles=16)
+    _log(f"decode beyond the LDS block buffer: lengths {lens}")
+    got = run_decode(csa2, wl)
+    refs = oracle.decode(wl)
+    judge(wl, got, refs)
+    dw = upload(wl)
+    kept, n_kept, _ = csa2.block_filter(dw.rg, dw.blk_sum, dw.q_idx, dw.w, n_keep=64)
+    assert np.array_equal(kept.cpu().numpy(), got["kept"]) and np.array_equal(n_kept.cpu().numpy(), got["n_kept"])
