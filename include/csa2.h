@@ -196,9 +196,10 @@ size_t csa2_sparse_attn_workspace_size(const csa2_ragged* rg, int32_t sel_ld);
 #define CSA2_QP_BF16  0
 #define CSA2_QP_MXFP8 1
 
-/* The whole path on one stream: (2a) and (1), then (2b), then (3).  With paged pools the
- * fine top-k also writes the picks' pool rows into the workspace (address translation
- * fused into the selection) and attention reads those. */
+/* The whole path on one stream: (2a) and (1), then (2b), then (3).  The fine top-k also
+ * writes the picks' pool rows into the workspace (for paged pools this is the address
+ * translation, fused into the selection; contiguous pools need total_entries < 2^31 for
+ * it) and attention reads those, so it needs no request offsets before its first reads. */
 typedef struct csa2_decode_args {
   csa2_ragged rg;
   const uint8_t* idx_k;        /* [total_entries][68] */
