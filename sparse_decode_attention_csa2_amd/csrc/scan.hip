@@ -21,6 +21,7 @@ constexpr int kWaves = 4;
 constexpr int kGroups = 4;                          // 16-entry groups per wave per tile
 constexpr int kTile = kWaves * kGroups * 16;        // 256 entries (or blocks) per WG
 constexpr int kRsrcWord3 = 0x00020000;             // raw buffer descriptor, gfx9 family
+typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
 
 #ifndef CSA2_SCAN_DEPTH
 #define CSA2_SCAN_DEPTH 3
@@ -265,7 +266,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
         for (int i = 4 * (int)threadIdx.x; i < wg_n; i += 4 * kWaves * 64) {
           const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&wstage[t][i]);
           if (i + 4 <= wg_n) {
-            store16_a4(orow + i, v);
+            // A scan that only produces scores (PARTS 1) hands them to the caller: stream
+            // them past the caches.  In the decode chain the select reads them next.
+            if constexpr (PARTS == 1)
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4a4_t*>(orow + i));
+            else
+              store16_a4(orow + i, v);
           } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
