@@ -7,17 +7,20 @@
 // row computes one softmax over both key sets (K = V = the 512-dim latent):
 //   z_i = sm_scale * q_h . x_i,  out_h = sum_i softmax(z)_i x_i,  lse_h = log sum_i e^z_i.
 //
-// Kernel structure.  A workgroup (4 waves) takes a range of 32-key tiles of one row.
-// Each thread owns two keys x 32 dims of a tile: it loads their records one tile ahead
-// (the loads of tile j+1 are in flight while tile j computes) and dequantises them
-// exactly to bf16 into LDS twice: key-major Kl[key][dim] for S^T = K Q^T and dim-major
-// Vt[dim][key] (the two keys packed per 32-bit word) for O^T = V^T P^T.  Window tokens
-// enter as their exact E4M3 values; their fp32 scale multiplies the logits and the
-// probabilities instead.  Wave w owns heads 16w..16w+15 (query fragments stay in
-// registers for all tiles); both products run on bf16 16x16x32 MFMAs with fp32
-// accumulation, with an online softmax between them.  Workgroups of one row write
-// (unnormalised O, running max, running sum) partials that a second kernel merges by
-// log-sum-exp; with a single split the kernel writes the result directly.
+// Kernel structure.  A workgroup of 8 waves takes a range of 64-key tiles of one row.
+// Per tile, each thread owns two keys x 32 dims: it loads their records during the
+// previous tile (the positions first, then the records, all addresses clamped so no
+// load waits on a branch) and dequantises them exactly to bf16 into one key-major LDS
+// copy Kl[key][dim].  Wave (hg, dh) owns heads 16hg..16hg+15 and latent dims
+// 256dh..256dh+255: it contracts its half of the dims for S^T = K Q^T (query fragments
+// stay in registers for all tiles) and the two halves meet through LDS; O^T = V^T P^T
+// reads its V^T operand from the same key-major copy with transposing LDS loads.
+// Window tokens enter as their exact E4M3 values; their fp32 scale multiplies the
+// logits and the probabilities instead.  Both products run on bf16 16x16x32 MFMAs with
+// fp32 accumulation and an online softmax between them; probabilities enter PV as
+// bf16 hi + lo parts.  Workgroups of one row write (unnormalised O, running max,
+// running sum) partials that a second kernel merges by log-sum-exp; with a single
+// split the kernel writes the result directly.
 #include <math.h>
 
 #include "csa2_internal.h"
