@@ -196,11 +196,11 @@ def read_counter_summary(name: str) -> dict:
     return out
 
 
-def graph_kernel_ms(hip, fns, replays: int) -> float:
+def graph_kernel_ms(hip, fns, replays: int, repeats: int = 5) -> float:
     """Average duration of one launch chain of fns, from a HIP event pair on the launch
-    stream around n back-to-back launches.  The stream is held by a spin kernel while
-    the launches are enqueued, so the GPU runs them back to back and the events do not
-    include host submission time."""
+    stream around n back-to-back launches; the median over `repeats` such runs.  The
+    stream is held by a spin kernel while the launches are enqueued, so the GPU runs
+    them back to back and the events do not include host submission time."""
     import torch
     n = max(8, min(400, replays * len(fns)))
     for f in fns[:4]:
@@ -208,13 +208,16 @@ def graph_kernel_ms(hip, fns, replays: int) -> float:
     torch.cuda.synchronize()
     ev = make_events(hip, 2)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    torch.cuda._sleep(int(2.0e9 * (n * 60e-6 + 2e-3)))
-    hip.hipEventRecord(ev[0], st)
-    for i in range(n):
-        fns[i % len(fns)]()
-    hip.hipEventRecord(ev[1], st)
-    torch.cuda.synchronize()
-    return elapsed_ms(hip, ev[0], ev[1]) / n
+    runs = []
+    for _ in range(repeats):
+        torch.cuda._sleep(int(2.0e9 * (n * 60e-6 + 2e-3)))
+        hip.hipEventRecord(ev[0], st)
+        for i in range(n):
+            fns[i % len(fns)]()
+        hip.hipEventRecord(ev[1], st)
+        torch.cuda.synchronize()
+        runs.append(elapsed_ms(hip, ev[0], ev[1]) / n)
+    return float(np.median(runs))
 
 
 def measure_decode(csa2, hip, wl, steps: int, warmup: int, max_reps: int = 128, qp_route: int = 0):
