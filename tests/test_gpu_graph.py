@@ -1,5 +1,5 @@
-"""Graph replay of the decode chain equals eager execution, replay after replay
-(needs an MI355X)."""
+"""Graph replay of the decode chain equals eager execution, replay after replay, and
+decoders on concurrent streams equal their lone runs (needs an MI355X)."""
 import os
 
 import numpy as np
@@ -48,3 +48,31 @@ def test_graph_replay_matches_eager(csa2):
             assert torch.equal(a, b), f"replay {it} differs from eager"
     for a, b in zip(_snap(o), ref_o):
         assert torch.equal(a, b)
+
+
+def test_concurrent_streams_with_own_workspaces(csa2):
+    # The entry points keep no state and allocate nothing, so two decoders (each with its
+    # own outputs and workspace) enqueued on two streams at once give the results each
+    # gives alone.
+    wa, wb = make_config(2), make_config(3)
+    da, db = upload(wa), upload(wb)
+    a = csa2.Decoder(*da.decode_inputs(), sm_scale=wa.sm_scale)
+    b = csa2.Decoder(*db.decode_inputs(), sm_scale=wb.sm_scale)
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    ref_a, ref_b = _snap(a), _snap(b)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        for d in (a, b):
+            for t in (d.out, d.lse, d.sel_idx, d.kept):
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            a.run(stream=sa.cuda_stream)
+            b.run(stream=sb.cuda_stream)
+        torch.cuda.synchronize()
+        for x, y in zip(_snap(a), ref_a):
+            assert torch.equal(x, y)
+        for x, y in zip(_snap(b), ref_b):
+            assert torch.equal(x, y)
