@@ -133,14 +133,14 @@ def touched_bytes(wl) -> int:
     return (wl.total_entries * 68 + int(wl.block_off[-1]) * 256 + R * (512 * 288 + 128 * 516 + 64 * 512 * 2))
 
 
-def algorithmic(wl):
-    """Algorithmic bytes / flops per launch of each stage."""
-    R = wl.num_rows
-    nb = int(wl.block_off[-1])
-    scan = wl.total_entries * 68 + nb * 256 + R * (8 * 128 * 2 + 8 * 4)
-    attn_bytes = R * (512 * 288 + 128 * (512 + 4) + 64 * 512 * 2 + 64 * 512 * 4 + 64 * 4)
-    attn_flops = R * 4 * 64 * (512 + 128) * 512
-    return scan, attn_bytes, attn_flops
+def step_bytes(wl) -> int:
+    """Algorithmic bytes of one decode step: every request's indexer keys (68 B per entry)
+    and block summaries (256 B per 64-entry block), each row's indexer query and weights,
+    and per row the attention's 512 selected records, 128 window tokens, query and
+    outputs.  The select's reads (at most 4,160 scores per row) are left out."""
+    nb = sum((wl.n_entries(b) + 63) // 64 for b in range(wl.num_requests))
+    ne = sum(wl.n_entries(b) for b in range(wl.num_requests))
+    return ne * 68 + nb * 256 + wl.num_rows * (8 * 128 * 2 + 8 * 4) + attn_bytes(wl)
 
 
 def cpu_baseline(wl, seconds: float):
@@ -475,6 +475,9 @@ def main() -> int:
         "stages_us_eager": m["stages_us_eager"],
         "step_latency_us": m["step_latency_us"],
         "kernels_headline": head,
+        "step_bytes": step_bytes(wl),
+        "step_GBs": step_bytes(wl) / (m["ms_per_step"] * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": step_bytes(wl) / (m["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "wall_s_timed": m["wall_s_timed"],
     }
     if not args.no_scale:
@@ -503,10 +506,12 @@ def main() -> int:
             w = mk()
             mi = measure_decode(csa2, hip, w, steps=max(64, min(K, 400)), warmup=8, qp_route=route)
             name = w.name + ("_mxfp8" if route == csa2.QP_MXFP8 else "")
+            gbs = step_bytes(w) / (mi["ms_per_step"] * 1e-3) / 1e9
             per[name] = {"requests": w.num_requests, "rows": w.num_rows, "entries": w.total_entries,
                            "paged": w.page_table is not None, "row_len": w.row_len is not None,
                            "qp_route": "mxfp8" if route == csa2.QP_MXFP8 else "bf16",
                            "rows_per_s": mi["rows_per_s"], "ms_per_step": mi["ms_per_step"],
+                           "step_bytes": step_bytes(w), "step_GBs": gbs, "step_frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
                            "step_latency_us": mi["step_latency_us"],
                            "stages_us_eager": mi["stages_us_eager"], "input_replicas": mi["input_replicas"]}
             del mi, w
