@@ -80,29 +80,11 @@ def replicate(dw, n):
     return reps
 
 
-def graph_time_ms(hip, fns, replays: int, warm: int = 2) -> float:
-    """Capture fns (each enqueues one launch chain) into one HIP graph, replay it, and
-    return the mean time per fn call from events recorded on the stream around the
-    replays."""
-    import torch
-    from sparse_decode_attention_csa2_amd import capture_calls
-    g = capture_calls(fns)
-    for _ in range(warm):
-        g.replay()
-    torch.cuda.synchronize()
-    ev = make_events(hip, 2)
-    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    hip.hipEventRecord(ev[0], st)
-    for _ in range(replays):
-        g.replay()
-    hip.hipEventRecord(ev[1], st)
-    torch.cuda.synchronize()
-    return elapsed_ms(hip, ev[0], ev[1]) / (replays * len(fns))
-
-
 def cache_write_timing(csa2, hip) -> dict:
     """csa2_cache_write (pooling, RMSNorm, FP4 quantisation, record and summary writes)
-    for the verify batch (8 requests x 6 rows) and for 64 requests x 2 rows, graph-timed."""
+    for the verify batch (8 requests x 6 rows) and for 64 requests x 2 rows: back-to-back
+    calls behind a spin kernel (one call is too short for a graph replay per call to
+    measure anything but the replay's own launch cost)."""
     import torch
     from synth import make_config, make_write_inputs
     from synth.device import upload
@@ -119,7 +101,7 @@ def cache_write_timing(csa2, hip) -> dict:
                 dev(w["gamma_kv"]), dev(w["gamma_idx"]), dw.main_kv, dw.idx_k, dw.blk_sum)
         csa2.cache_write(*args)
         torch.cuda.synchronize()
-        ms = graph_time_ms(hip, [lambda: csa2.cache_write(*args)], replays=200)
+        ms = graph_kernel_ms(hip, [lambda: csa2.cache_write(*args)], replays=200)
         entries = int(sum(1 for p in w["row_pos"] if p % 2 == 1))
         out[name] = {"rows": wl.num_rows, "entries_written": entries, "us_per_call": ms * 1e3}
         del dw, args

@@ -172,27 +172,44 @@ __global__ __launch_bounds__(64) void k_write_summaries(WriteArgs a) {
   int64_t e0, n, bl0, nb;
   req_entries(a.g, b, e0, n);
   req_blocks(a.g, b, n, bl0, nb);
-  int64_t tmin = -1, tmax = -1;
-  for (int r = r0; r < r1; ++r) {
-    const int64_t t = row_entry(a, r, b, n);
-    if (t >= 0) {
-      tmin = tmin < 0 ? t : (t < tmin ? t : tmin);
-      tmax = t > tmax ? t : tmax;
-    }
+  // Lane l looks at row r0 + l (a request has at most 16 rows): one load round for all.
+  static_assert(CSA2_ROWS_PER_REQ_MAX <= 64, "one row per lane");
+  const int64_t tl = r0 + lane < r1 ? row_entry(a, r0 + lane, b, n) : -1;
+  int64_t tmin = tl >= 0 ? tl : INT64_MAX, tmax = tl;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int64_t om = __shfl_xor(tmin, m, 64), ox = __shfl_xor(tmax, m, 64);
+    tmin = om < tmin ? om : tmin;
+    tmax = ox > tmax ? ox : tmax;
   }
+  if (tmin == INT64_MAX) tmin = -1;
   if (tmin >= 0) {
     const int64_t j = tmin / CSA2_BLOCK + which;
     if (j <= tmax / CSA2_BLOCK && j < nb) {
       const int cnt = (int)min<int64_t>(CSA2_BLOCK, n - j * CSA2_BLOCK);
+      // A block's entries are consecutive pool rows (a page, with paged pools).  Their
+      // bytes are loaded kB at a time (independent loads, clamped to the block's last
+      // entry) and summed in entry order.
+      const uint8_t* blk = a.idx_k + entry_row(a.g, b, e0, j * CSA2_BLOCK) * CSA2_IDX_BYTES;
+      constexpr int kB = 64;
       double s0 = 0.0, s1 = 0.0;
-      for (int e = 0; e < cnt; ++e) {
-        const uint8_t* rec = a.idx_k + entry_row(a.g, b, e0, j * CSA2_BLOCK + e) * CSA2_IDX_BYTES;
-        const uint32_t c = rec[lane];
-        const uint32_t sb = rec[64 + lane / 16];
-        // E2M1 value of each nibble times the E8M0 scale (exact in double).
-        const double sc = ldexp(1.0, (int)sb - 127);
-        s0 += e2m1_value(c & 15u) * sc;
-        s1 += e2m1_value(c >> 4) * sc;
+      for (int eb = 0; eb < cnt; eb += kB) {
+        uint32_t c[kB], sb[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const uint8_t* rec = blk + min(eb + u, cnt - 1) * CSA2_IDX_BYTES;
+          c[u] = rec[lane];
+          sb[u] = rec[64 + lane / 16];
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          if (eb + u < cnt) {
+            // E2M1 value of each nibble times the E8M0 scale (exact in double).
+            const double sc = ldexp(1.0, (int)sb[u] - 127);
+            s0 += e2m1_value(c[u] & 15u) * sc;
+            s1 += e2m1_value(c[u] >> 4) * sc;
+          }
+        }
       }
       const uint32_t w = bf16_rne_from_double(s0 / cnt) | (bf16_rne_from_double(s1 / cnt) << 16);
       *reinterpret_cast<uint32_t*>(a.blk_sum + block_row(a.g, b, bl0, j) * CSA2_IDX_D + 2 * lane) = w;
