@@ -407,7 +407,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   // Split partial layout [split][wave = hg + 4 dh][16 d-tiles][lane][4].
   const float* src = a.opart + ((base * 8 + w + 4 * (t >> 4)) * 16 + (t & 15)) * 256 + 4 * lane;
   constexpr int64_t kStride = 8 * 16 * 256;   // floats per split
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;   // one round of loads covers a one-row launch (10 splits)
   f32x4_t v[kBatch];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u)   // every launched split has a partial slot; only u < ns are used
