@@ -147,3 +147,31 @@ def test_decode_beyond_lds_block_buffer(csa2):
     dw = upload(wl)
     kept, n_kept, _ = csa2.block_filter(dw.rg, dw.blk_sum, dw.q_idx, dw.w, n_keep=64)
     assert np.array_equal(kept.cpu().numpy(), got["kept"]) and np.array_equal(n_kept.cpu().numpy(), got["n_kept"])
+
+
+def test_bench_scale_batches_on_sampled_rows(csa2):
+    # The two 285 MB batches bench.py times the scan on (64 x 65,536 entries, 4 chunks per
+    # wave; 4 x 1,048,576 entries), in the launch configuration it times: the full-scan
+    # scores of sampled requests, and whole decode rows of the 64-request batch.
+    from synth import make_config as mk
+    wl = mk(5)
+    _log(f"64 x 128K batch: {wl.total_entries} entries")
+    dw = upload(wl)
+    scores = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
+    for b in (0, 17, 42, 63):
+        ref = oracle.request_scores(wl, b)[0]
+        err = np.abs(scores[b, :wl.n_entries(b)] - ref).max() / np.abs(ref).mean()
+        assert err <= 1e-5, f"request {b}: score error {err:.3g}"
+    rows = [0, 31, 63]
+    got = run_decode(csa2, wl)
+    refs = oracle.decode(wl, rows=rows)
+    judge(wl, got, refs, rows=rows)
+    del dw, wl
+    torch.cuda.empty_cache()
+    w4 = mk(4, scan_only=True)
+    d4 = upload(w4)
+    s4 = csa2.index_score(d4.rg, d4.idx_k, d4.q_idx, d4.w).cpu().numpy()
+    for b in (0, 3):
+        ref = oracle.request_scores(w4, b)[0]
+        err = np.abs(s4[b, :w4.n_entries(b)] - ref).max() / np.abs(ref).mean()
+        assert err <= 1e-5, f"1M request {b}: score error {err:.3g}"
