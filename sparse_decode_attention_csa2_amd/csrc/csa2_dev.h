@@ -76,6 +76,10 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8_t& hi, 
 // 448.  The rounding is done in fp32 arithmetic (exact scalings, one round-to-nearest-
 // even of a value with the grid step brought to 1), not by a conversion instruction.
 // ---------------------------------------------------------------------------------
+#ifndef CSA2_MX_HW_CVT
+#define CSA2_MX_HW_CVT 1
+#endif
+
 __device__ __forceinline__ int mx8_scale_exp(float amax) {
   if (!(amax > 0.f)) return -127;
   const int e = __builtin_amdgcn_frexp_expf(amax) - 1;   // floor(log2(amax)), subnormals included
@@ -102,9 +106,23 @@ __device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) 
   amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
   const int s = mx8_scale_exp(amax);
   u32x4_t w;
+#if CSA2_MX_HW_CVT
+  // gfx950's scaled FP8 conversions: x / 2^s to E4M3FN (round to nearest even) and back
+  // times 2^s, after clamping to the largest grid value (448 units) so nothing overflows.
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const float sc = __builtin_ldexpf(1.f, s), lim = __builtin_ldexpf(448.f, s);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = fminf(fmaxf(v[2 * q], -lim), lim), b = fminf(fmaxf(v[2 * q + 1], -lim), lim);
+    const v2s p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, sc, false);
+    const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)__builtin_bit_cast(int, p), sc, false);
+    w[q] = bf16_bits_rne(f[0]) | (bf16_bits_rne(f[1]) << 16);
+  }
+#else
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     w[q] = bf16_bits_rne(mx8_round(v[2 * q], s)) | (bf16_bits_rne(mx8_round(v[2 * q + 1], s)) << 16);
+#endif
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
