@@ -242,7 +242,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
 #pragma unroll
       for (int d = 0; d < kDepth; ++d)
         if (d < iters && lb0 + d * kStep < wg_n) issue(ring[d], lb0 + d * kStep);
+      // Both parts in one launch: the workgroup's own 64-entry blocks (4 x iters <= 16,
+      // one MFMA group) are scored by wave 0, their summaries loaded with its first
+      // chunk.
+      bf16x8_t kbs[4];
+      int64_t jb0 = 0, jend = 0;
+      if constexpr (PARTS == 3) {
+        if (wave == 0) {
+          int64_t bl0, nb;
+          req_blocks(a.g, b, n, bl0, nb, PAGED);
+          jb0 = wg_base / CSA2_BLOCK;
+          jend = min<int64_t>(nb, (wg_base + wg_n + CSA2_BLOCK - 1) / CSA2_BLOCK);
+          const int64_t j = jb0 + m;
+          const int64_t jl = j < jend ? j : (jend > 0 ? jend - 1 : 0);
+          const int64_t row = PAGED ? page_of(a.g, b, jl) : bl0 + jl;
+          const uint16_t* sp = a.blk_sum + row * CSA2_IDX_D + 32 * g;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kbs[c] = as_bf16x8(load16(sp + 8 * c));
+        }
+      }
       load_query<MAXPAIRS>(a, r0, r1, qa, wv);
+      if constexpr (PARTS == 3) {
+        if (wave == 0) score_group<MAXPAIRS>(kbs, qa, wv, npairs, r0, r1, jb0 + m, jend, a.blk_scores, a.blk_ld);
+      }
       for (int c0 = 0; c0 < iters; c0 += kDepth) {
         bool done = false;
 #pragma unroll
@@ -384,7 +406,8 @@ hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool bloc
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;
   a.blk_groups = iters < kGroups ? iters : kGroups;
   const int64_t blk_tile = (int64_t)kWaves * 16 * a.blk_groups;
-  a.block_tiles = blocks ? (int32_t)((max_nb + blk_tile - 1) / blk_tile) : 0;
+  // With both parts, the entry workgroups score their own blocks (no block tiles).
+  a.block_tiles = (blocks && !entries) ? (int32_t)((max_nb + blk_tile - 1) / blk_tile) : 0;
   const int gx = a.entry_tiles + a.block_tiles;
   if (gx == 0 || a.g.B == 0 || a.g.R == 0) return hipSuccess;
   const dim3 grid(gx, a.g.B);
