@@ -150,8 +150,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
 
-  // Block-summary tiles come first in the grid so that they start early and do not
-  // trail the (many more) entry tiles.
+  // Block-summary tiles (launches that score only the summaries) come first in the grid;
+  // launches that also score entries have none (their entry workgroups score their own
+  // blocks).
   if ((int)blockIdx.x >= a.block_tiles) {
     // A workgroup takes iters x 4 consecutive 64-entry chunks; on step c wave w scores
     // chunk 4c + w, so the four waves of a step read 17 KB of contiguous keys.  Each
