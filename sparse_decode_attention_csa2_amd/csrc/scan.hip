@@ -150,9 +150,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
 
-  // Block-summary tiles (launches that score only the summaries) come first in the grid;
-  // launches that also score entries have none (their entry workgroups score their own
-  // blocks).
+  // Block-summary tiles come first in the grid so that they start early and do not
+  // trail the (many more) entry tiles.  Some launches that also score entries have none:
+  // their entry workgroups score their own blocks (see launch_scan).
   if ((int)blockIdx.x >= a.block_tiles) {
     // A workgroup takes iters x 4 consecutive 64-entry chunks; on step c wave w scores
     // chunk 4c + w, so the four waves of a step read 17 KB of contiguous keys.  Each
@@ -243,13 +243,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
 #pragma unroll
       for (int d = 0; d < kDepth; ++d)
         if (d < iters && lb0 + d * kStep < wg_n) issue(ring[d], lb0 + d * kStep);
-      // Both parts in one launch: the workgroup's own 64-entry blocks (4 x iters <= 16,
-      // one MFMA group) are scored by wave 0, their summaries loaded with its first
-      // chunk.
+      // Both parts in one launch without block tiles: the workgroup's own 64-entry
+      // blocks (4 x iters <= 16, one MFMA group) are scored by wave 0, their summaries
+      // loaded with its first chunk.
       bf16x8_t kbs[4];
       int64_t jb0 = 0, jend = 0;
+      const bool own_blocks = PARTS == 3 && a.block_tiles == 0 && wave == 0;   // uniform per wave
       if constexpr (PARTS == 3) {
-        if (wave == 0) {
+        if (own_blocks) {
           int64_t bl0, nb;
           req_blocks(a.g, b, n, bl0, nb, PAGED);
           jb0 = wg_base / CSA2_BLOCK;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
       }
       load_query<MAXPAIRS>(a, r0, r1, qa, wv);
       if constexpr (PARTS == 3) {
-        if (wave == 0) score_group<MAXPAIRS>(kbs, qa, wv, npairs, r0, r1, jb0 + m, jend, a.blk_scores, a.blk_ld);
+        if (own_blocks) score_group<MAXPAIRS>(kbs, qa, wv, npairs, r0, r1, jb0 + m, jend, a.blk_scores, a.blk_ld);
       }
       for (int c0 = 0; c0 < iters; c0 += kDepth) {
         bool done = false;
@@ -407,8 +408,12 @@ hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool bloc
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;
   a.blk_groups = iters < kGroups ? iters : kGroups;
   const int64_t blk_tile = (int64_t)kWaves * 16 * a.blk_groups;
-  // With both parts, the entry workgroups score their own blocks (no block tiles).
-  a.block_tiles = (blocks && !entries) ? (int32_t)((max_nb + blk_tile - 1) / blk_tile) : 0;
+  // With both parts, the entry workgroups score their own blocks instead of separate
+  // block tiles when their workgroups are long (4 chunks per wave) or hold several row
+  // pairs (where the block tiles would push the grid past one round of workgroups);
+  // short one-row workgroups keep the block tiles off their critical path.
+  const bool own_blocks = entries && blocks && (iters >= kMaxIters || max_rows_per_req > 2);
+  a.block_tiles = (blocks && !own_blocks) ? (int32_t)((max_nb + blk_tile - 1) / blk_tile) : 0;
   const int gx = a.entry_tiles + a.block_tiles;
   if (gx == 0 || a.g.B == 0 || a.g.R == 0) return hipSuccess;
   const dim3 grid(gx, a.g.B);
