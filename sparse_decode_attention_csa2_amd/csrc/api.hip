@@ -395,9 +395,16 @@ int csa2_sparse_attn(const csa2_ragged* rg, const uint16_t* q, const uint8_t* ma
 }
 
 // Workspace of csa2_decode, in carve order.
+struct SliceBufs {
+  int32_t n_slices = 0;
+  int32_t* blk = nullptr;
+  float* sc = nullptr;
+  int32_t* n = nullptr;
+};
+
 static size_t decode_layout(const csa2_decode_args* a, char* base, float** scores, float** blk_scores,
                             int32_t** kept, int32_t** n_kept, int32_t** sel, int32_t** n_sel, int32_t** sel_rows,
-                            char** attn_ws, size_t* attn_bytes) {
+                            char** attn_ws, size_t* attn_bytes, SliceBufs* slices = nullptr) {
   const csa2_ragged& rg = a->rg;
   const int64_t R = rg.num_rows;
   const int64_t ld = round_up((size_t)(rg.max_entries > 0 ? rg.max_entries : 1), 64);
@@ -424,6 +431,15 @@ static size_t decode_layout(const csa2_decode_args* a, char* base, float** score
   char* aw = c.take<char>(ab);
   if (attn_ws) *attn_ws = aw;
   if (attn_bytes) *attn_bytes = ab;
+  // Sliced coarse stage (full scans of rows with many blocks).
+  const int32_t nsl = a->scan_mode == 0 ? select_slices(blocks_of(rg.max_entries), a->n_keep) : 0;
+  if (nsl > 0) {
+    const size_t cand = (size_t)R * nsl * a->n_keep;
+    int32_t* cb = c.take<int32_t>(cand);
+    float* cs = c.take<float>(cand);
+    int32_t* cn = c.take<int32_t>((size_t)R * nsl);
+    if (slices) *slices = SliceBufs{nsl, cb, cs, cn};
+  }
   return round_up(c.used, 256);
 }
 
@@ -461,8 +477,9 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   int32_t *kept, *n_kept, *sel, *n_sel, *sel_rows;
   char* attn_ws;
   size_t attn_bytes;
+  SliceBufs slices;
   decode_layout(a, static_cast<char*>(ws), &scores, &blk_scores, &kept, &n_kept, &sel, &n_sel, &sel_rows, &attn_ws,
-                &attn_bytes);
+                &attn_bytes, &slices);
   const int64_t ld = a->scores ? a->scores_ld : (int64_t)round_up((size_t)(g.max_entries > 0 ? g.max_entries : 1), 64);
   const int64_t blk_ld = (int64_t)round_up((size_t)(blocks_of(g.max_entries) > 0 ? blocks_of(g.max_entries) : 1), 64);
 
@@ -501,6 +518,10 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   se.sel = sel;
   se.n_sel = n_sel;
   se.sel_rows = sel_rows;
+  se.n_slices = slices.n_slices;
+  se.cand_blk = slices.blk;
+  se.cand_sc = slices.sc;
+  se.cand_n = slices.n;
 
   auto mark = [&](int i) -> hipError_t {
     return a->events ? hipEventRecord(static_cast<hipEvent_t>(a->events[i]), st) : hipSuccess;
@@ -510,6 +531,8 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
     // One launch scores every entry and every block summary; one launch selects.
     LAUNCH(launch_scan(sa, a->rg.max_rows_per_request, true, true, st), "scan");
     LAUNCH(mark(1), "event record");
+    // Rows with many blocks: slices of blocks are ranked in parallel first.
+    LAUNCH(launch_block_slices(se, st), "block slices");
     LAUNCH(launch_select_fused(se, st), "select");
   } else {
     // Coarse stage first, then score only the kept blocks' entries.

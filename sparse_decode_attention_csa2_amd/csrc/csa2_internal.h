@@ -146,11 +146,29 @@ struct SelectArgs {
   int32_t* n_sel;            // [R]
   float* sel_score;          // nullable [R][k]
   int32_t* sel_rows;         // nullable [R][k]: pool rows of the selected entries (-1 pad)
+  // Sliced coarse stage (many blocks per row): slice s of row r keeps its n_keep best
+  // blocks in cand_blk / cand_sc [R][n_slices][n_keep] (ascending), cand_n [R][n_slices].
+  int32_t n_slices;          // 0: the coarse stage ranks all of a row's blocks at once
+  int32_t* cand_blk;
+  float* cand_sc;
+  int32_t* cand_n;
 };
+
+// Blocks per slice of the sliced coarse stage, and when it is used: rows with more than
+// kSelSliceFrom blocks, as long as the candidates fit the select's key buffer.
+constexpr int kSelSlice = 2048;
+constexpr int kSelSliceFrom = 4096;
+constexpr int kSelSliceCand = 4096;
+inline int32_t select_slices(int64_t max_nb, int32_t n_keep) {
+  if (max_nb <= kSelSliceFrom) return 0;
+  const int64_t s = (max_nb + kSelSlice - 1) / kSelSlice;
+  return s * n_keep <= kSelSliceCand ? (int32_t)s : 0;
+}
 
 hipError_t launch_block_select(SelectArgs a, hipStream_t st);
 hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st);
 hipError_t launch_select_fused(SelectArgs a, hipStream_t st);
+hipError_t launch_block_slices(SelectArgs a, hipStream_t st);
 
 struct AttnArgs {
   RaggedDev g;

@@ -37,6 +37,7 @@ constexpr int kLdsBlocks = 16384;                            // block keys held 
 constexpr int kGB = 16;                                      // gather batch per thread
 static_assert(kMaxCand >= CSA2_TOPK_ALL_MAX, "candidate buffer");
 static_assert(kLdsBlocks >= kMaxCand, "shared key buffer");
+static_assert(kLdsBlocks >= kSelSliceCand && kSelSlice % kWave == 0, "sliced coarse stage buffers");
 
 struct SelShared {
   alignas(16) uint32_t hist[2][kBins];
@@ -407,6 +408,42 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
   if (threadIdx.x == 0) sh.nk = cnt;
 }
 
+// Sliced coarse stage, second level: rank the slices' candidates for row r (slot-major,
+// which is ascending block order, so ties still go to the lower block) and keep the
+// n_keep best plus the newest block, as coarse() does for all blocks at once.  The
+// n_keep best of a row are among the n_keep best of their slices.
+__device__ void coarse_cand(const SelectArgs& a, int r, int nb, SelShared& sh, uint32_t* kbuf) {
+  int32_t* kout = a.kept ? a.kept + (int64_t)r * a.kept_ld : nullptr;
+  const int K = a.n_keep, items = a.n_slices * K;
+  const float* cs = a.cand_sc + (int64_t)r * items;
+  const int32_t* cb = a.cand_blk + (int64_t)r * items;
+  const int32_t* cn = a.cand_n + (int64_t)r * a.n_slices;
+  if (threadIdx.x == 0) sh.flag = 0;
+  auto emit = [&](int pos, int i) {
+    const int blk = cb[i];
+    sh.kl[pos] = blk;
+    if (kout) kout[pos] = blk;
+    if (blk == nb - 1) sh.flag = 1;
+  };
+  gather(items, [&](int i) { return i % K < cn[i / K]; }, [&](int i, bool ok) { return cs[ok ? i : 0]; }, kbuf,
+         sh);
+  __syncthreads();
+  int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), K, sh, emit);
+  __syncthreads();
+  if (nb > 0 && a.keep_newest && sh.flag == 0) {
+    if (threadIdx.x == 0) {
+      sh.kl[cnt] = nb - 1;
+      if (kout) kout[cnt] = nb - 1;
+    }
+    ++cnt;
+  }
+  if (kout) {
+    for (int i = cnt + threadIdx.x; i < a.kept_ld; i += NT) kout[i] = -1;
+    if (threadIdx.x == 0) a.n_kept[r] = cnt;
+  }
+  if (threadIdx.x == 0) sh.nk = cnt;
+}
+
 // Fine stage of row r over the kept blocks sh.kl[0 .. nk) (chunk s = kept block s,
 // lane = entry) or, with all_entries, over entries 0 .. n-1.  Candidates are the items
 // with a key: positions the row sees whose score is not NaN.  When a.sel_rows is set
@@ -494,17 +531,48 @@ __global__ __launch_bounds__(NT) void k_topk(SelectArgs a, int all_entries) {
   fine<PAGED>(a, r, n, e0, nk, all_entries != 0, sh, kbuf);
 }
 
+// Sliced coarse stage, first level: workgroup (s, r) ranks blocks s*kSelSlice ..
+// of row r and writes its n_keep best (ascending) with their scores.
+template <bool PAGED>
+__global__ __launch_bounds__(NT) void k_block_slices(SelectArgs a) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t kbuf[kSelSlice];
+  const int s = blockIdx.x, r = blockIdx.y;
+  int64_t n, e0;
+  const int nb = row_blocks<PAGED>(a, r, n, e0);
+  const int j0 = s * kSelSlice;
+  const int items = min(kSelSlice, nb - j0);
+  const int64_t slot = ((int64_t)r * a.n_slices + s) * a.n_keep;
+  if (items <= 0) {
+    if (threadIdx.x == 0) a.cand_n[(int64_t)r * a.n_slices + s] = 0;
+    return;
+  }
+  const float* bs = a.blk_scores + (int64_t)r * a.blk_ld + j0;
+  gather(items, [](int) { return true; }, [&](int i, bool ok) { return bs[ok ? i : 0]; }, kbuf, sh);
+  __syncthreads();
+  const int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), a.n_keep, sh, [&](int pos, int i) {
+    a.cand_blk[slot + pos] = j0 + i;
+    a.cand_sc[slot + pos] = key_score(kbuf[i]);
+  });
+  if (threadIdx.x == 0) a.cand_n[(int64_t)r * a.n_slices + s] = cnt;
+}
+
 // Both stages for one row; the block keys and the candidate keys share one LDS buffer.
-template <bool PAGED, bool BIG>
+// CMODE 0: all blocks ranked from LDS (first batch prefetched); 1: rows may have more
+// blocks than LDS holds; 2: the sliced coarse stage's candidates.
+template <bool PAGED, int CMODE>
 __global__ __launch_bounds__(NT) void k_select_fused(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
   const int r = blockIdx.x;
   float pre[kGB];
-  if (!BIG) prefetch_blocks(a, r, pre);
+  if (CMODE == 0) prefetch_blocks(a, r, pre);
   int64_t n, e0;
   const int nb = row_blocks<PAGED>(a, r, n, e0);
-  coarse<BIG>(a, r, nb, sh, kbuf, pre);
+  if (CMODE == 2)
+    coarse_cand(a, r, nb, sh, kbuf);
+  else
+    coarse<CMODE == 1>(a, r, nb, sh, kbuf, pre);
   __syncthreads();
   fine<PAGED>(a, r, n, e0, sh.nk, false, sh, kbuf);
 }
@@ -534,13 +602,27 @@ hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st) {
 
 hipError_t launch_select_fused(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  const bool big = a.blk_ld > kLdsBlocks;
+  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : 0);
+  const dim3 grid(a.g.R), block(NT);
+  if (a.g.page_table) {
+    if (mode == 2) k_select_fused<true, 2><<<grid, block, 0, st>>>(a);
+    else if (mode == 1) k_select_fused<true, 1><<<grid, block, 0, st>>>(a);
+    else k_select_fused<true, 0><<<grid, block, 0, st>>>(a);
+  } else {
+    if (mode == 2) k_select_fused<false, 2><<<grid, block, 0, st>>>(a);
+    else if (mode == 1) k_select_fused<false, 1><<<grid, block, 0, st>>>(a);
+    else k_select_fused<false, 0><<<grid, block, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_slices(SelectArgs a, hipStream_t st) {
+  if (a.g.R == 0 || a.n_slices == 0) return hipSuccess;
+  const dim3 grid(a.n_slices, a.g.R);
   if (a.g.page_table)
-    big ? k_select_fused<true, true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a)
-        : k_select_fused<true, false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+    k_block_slices<true><<<grid, dim3(NT), 0, st>>>(a);
   else
-    big ? k_select_fused<false, true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a)
-        : k_select_fused<false, false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a);
+    k_block_slices<false><<<grid, dim3(NT), 0, st>>>(a);
   return hipGetLastError();
 }
 
