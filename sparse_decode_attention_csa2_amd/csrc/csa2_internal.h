@@ -156,7 +156,10 @@ struct SelectArgs {
 
 // Blocks per slice of the sliced coarse stage, and when it is used: rows with more than
 // kSelSliceFrom blocks, as long as the candidates fit the select's key buffer.
-constexpr int kSelSlice = 2048;
+#ifndef CSA2_SEL_SLICE
+#define CSA2_SEL_SLICE 1024
+#endif
+constexpr int kSelSlice = CSA2_SEL_SLICE;
 constexpr int kSelSliceFrom = 4096;
 constexpr int kSelSliceCand = 4096;
 inline int32_t select_slices(int64_t max_nb, int32_t n_keep) {
