@@ -247,16 +247,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
       // blocks (4 x iters <= 16, one MFMA group) are scored by wave 0, their summaries
       // loaded with its first chunk.
       bf16x8_t kbs[4];
-      int64_t jb0 = 0, jend = 0;
-      const bool own_blocks = PARTS == 3 && a.block_tiles == 0 && wave == 0;   // uniform per wave
+      int64_t jb0 = 0, jend = 0, bl0 = 0;
+      bool own_blocks = PARTS == 3 && a.block_tiles == 0 && wave == 0;   // uniform per wave
       if constexpr (PARTS == 3) {
         if (own_blocks) {
-          int64_t bl0, nb;
+          int64_t nb;
           req_blocks(a.g, b, n, bl0, nb, PAGED);
           jb0 = wg_base / CSA2_BLOCK;
           jend = min<int64_t>(nb, (wg_base + wg_n + CSA2_BLOCK - 1) / CSA2_BLOCK);
+          // None of the workgroup's blocks in the pool: nothing to score (this also keeps
+          // the clamped row below in bounds).
+          own_blocks = jend > jb0;
+        }
+        if (own_blocks) {
           const int64_t j = jb0 + m;
-          const int64_t jl = j < jend ? j : (jend > 0 ? jend - 1 : 0);
+          const int64_t jl = j < jend ? j : jend - 1;
           const int64_t row = PAGED ? page_of(a.g, b, jl) : bl0 + jl;
           const uint16_t* sp = a.blk_sum + row * CSA2_IDX_D + 32 * g;
 #pragma unroll

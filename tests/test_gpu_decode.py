@@ -149,6 +149,28 @@ def test_decode_beyond_lds_block_buffer(csa2):
     assert np.array_equal(kept.cpu().numpy(), got["kept"]) and np.array_equal(n_kept.cpu().numpy(), got["n_kept"])
 
 
+def test_request_without_summaries_in_the_pool(csa2):
+    # block_off is clamped to the summary pool: a request whose summaries start at its end
+    # has no blocks to rank (nothing kept, nothing selected: attention over its window
+    # only), and the other requests are unaffected.  Three rows in request 0 make the one
+    # scan launch score each workgroup's own blocks, the path that clamps this case.
+    wl = make_workload("noblk", 51, [64 * 40 + 9, 64 * 12 + 5], rows_per_req=[3, 1], n_needles=4)
+    _log("request 1 with no summaries in the pool")
+    ref = run_decode(csa2, wl, k=256, n_keep=16)
+    end0 = int(wl.block_off[1])
+    wl.block_off = wl.block_off.copy()
+    wl.block_off[2] = end0
+    wl.blk_sum = wl.blk_sum[:end0].copy()   # the pool ends where request 1's summaries would start
+    got = run_decode(csa2, wl, k=256, n_keep=16)
+    for key in ("out", "lse", "sel", "kept", "n_sel", "n_kept"):
+        a, b = np.ascontiguousarray(got[key][:3]), np.ascontiguousarray(ref[key][:3])
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b), key
+    assert got["n_kept"][3] == 0 and got["n_sel"][3] == 0
+    assert (got["sel"][3] == -1).all() and (got["kept"][3] == -1).all()
+    assert np.isfinite(got["out"][3]).all() and np.isfinite(got["lse"][3]).all()
+
+
 def test_bench_scale_batches_on_sampled_rows(csa2):
     # The two 285 MB batches bench.py times the scan on (64 x 65,536 entries, 4 chunks per
     # wave; 4 x 1,048,576 entries), in the launch configuration it times: the full-scan
