@@ -387,6 +387,11 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 // thread), and the partial loads are issued before the statistics are combined.
 constexpr int kMaxSplits = (CSA2_K_MAX + CSA2_SWA_MAX + 31) / 32;
 
+// KB: partial loads issued in one round per thread (>= the launch's splits).  Launches
+// with at most 8 splits (many rows) take KB = 8: 64 VGPRs, 8 waves per SIMD, so a
+// 64-row launch's 2,048 workgroups are all resident at once (KB = 16 holds 82 VGPRs,
+// 5 waves per SIMD).
+template <int KB>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   touch_kernargs<sizeof(AttnArgs)>();
   __shared__ float msh[kMaxSplits][16], lsh[kMaxSplits][16];
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   // Split partial layout [split][wave = hg + 4 dh][16 d-tiles][lane][4].
   const float* src = a.opart + ((base * 8 + w + 4 * (t >> 4)) * 16 + (t & 15)) * 256 + 4 * lane;
   constexpr int64_t kStride = 8 * 16 * 256;   // floats per split
-  constexpr int kBatch = 16;   // one round of loads covers a one-row launch (10 splits)
+  constexpr int kBatch = KB;
   f32x4_t v[kBatch];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u)   // every launched split has a partial slot; only u < ns are used
@@ -484,7 +489,11 @@ hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0 || a.splits == 1) return hipSuccess;
-  k_attn_merge<<<dim3(32, a.g.R), dim3(256), 0, st>>>(a);
+  const dim3 grid(32, a.g.R), block(256);
+  if (a.splits <= 8)
+    k_attn_merge<8><<<grid, block, 0, st>>>(a);
+  else
+    k_attn_merge<16><<<grid, block, 0, st>>>(a);
   return hipGetLastError();
 }
 
