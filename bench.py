@@ -342,7 +342,7 @@ def scale_rooflines(csa2, hip, steps: int, profile_only: bool = False):
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
             "traffic": traffic, "traffic_note": traffic_note, "bytes_per_launch": sb, "us_per_launch": s_ms * 1e3,
             "plain_read_GBs": read_gbs, "frac_of_plain_read": gbs / read_gbs,
-            "plain_read_note": "csa2_debug_stream_read (16-B loads, 16 KiB per workgroup) over the same "
+            "plain_read_note": "csa2_debug_stream_read (non-temporal 16-B loads, 16 KiB per workgroup) over the same "
                                "285 MB, two alternating copies, same timing"}
     # The 1M-context batch (4 requests x 1,048,576 entries, 285 MB of keys).
     w4 = make_config(4, scan_only=True)

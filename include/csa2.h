@@ -279,8 +279,8 @@ int csa2_debug_mxfp8(const float* x, int64_t n, float* out, void* stream);
 
 /* Measurement hook, for callers that want the bandwidth a plain streaming read reaches
  * on this device (the reference the indexer scan is compared with): reads `bytes` bytes
- * at `src` (16-byte aligned, bytes a multiple of 16) with 16-byte loads, 16 KiB per
- * workgroup, and writes nothing unless the bytes' XOR equals an unlikely constant, in
+ * at `src` (16-byte aligned, bytes a multiple of 16) with non-temporal 16-byte loads,
+ * 16 KiB per workgroup, and writes nothing unless the bytes' XOR equals an unlikely constant, in
  * which case one word goes to `sink` (4 bytes of device memory).  Errors:
  * CSA2_ERR_INVALID_ARG for misaligned pointers or sizes. */
 int csa2_debug_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);

@@ -149,19 +149,21 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int kind, const uint8_t* 
 
 namespace csa2 {
 // Plain streaming read: workgroup w reads the 16 KiB chunk w with four 16-B loads per
-// thread in flight.
+// thread in flight, non-temporal (the fastest of the read patterns measured: chunks of
+// 8-64 KiB, 256 or 512 threads, persistent grids, with and without the hint).
 __global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__ p, int64_t n16, uint32_t* sink) {
   const int64_t b0 = (int64_t)blockIdx.x * 1024;
   const int64_t e = b0 + 1024 < n16 ? b0 + 1024 : n16;
   uint32_t acc = 0u;
   int64_t i = b0 + threadIdx.x;
   if (i + 768 < e) {
-    const u32x4_t x0 = p[i], x1 = p[i + 256], x2 = p[i + 512], x3 = p[i + 768];
+    const u32x4_t x0 = __builtin_nontemporal_load(p + i), x1 = __builtin_nontemporal_load(p + i + 256),
+                  x2 = __builtin_nontemporal_load(p + i + 512), x3 = __builtin_nontemporal_load(p + i + 768);
     const u32x4_t y = x0 ^ x1 ^ x2 ^ x3;
     acc = y[0] ^ y[1] ^ y[2] ^ y[3];
   } else {
     for (; i < e; i += 256) {
-      const u32x4_t x = p[i];
+      const u32x4_t x = __builtin_nontemporal_load(p + i);
       acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
     }
   }

@@ -138,7 +138,12 @@ __device__ __forceinline__ void flush_chunk(float (*sb)[64], int nrows, int r0, 
 // PARTS: 1 = entries only, 2 = block summaries only, 3 = both in one launch (distinct
 // instantiations keep the variants apart in kernel traces).  PAGED: the pools are
 // 64-entry pages reached through the page table (a chunk is exactly one page).
-template <int MAXPAIRS, int PARTS, bool PAGED>
+// LDSK: each wave reads its 64-entry chunk of keys as one contiguous 4,352-byte run of
+// whole cache lines, with the non-temporal hint, and regroups it into the MFMA layout
+// through LDS (otherwise lanes load that layout directly: 16-byte pieces 68 bytes
+// apart plus scale bytes, partial lines that the L2 completes across loads, which the
+// non-temporal hint defeats).
+template <int MAXPAIRS, int PARTS, bool PAGED, bool LDSK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS == 1 ? CSA2_SCAN_WAVES_PER_EU : (MAXPAIRS == 8 ? 1 : 2)))) void k_scan(ScanArgs a) {
   const int b = blockIdx.y;
   int64_t e0, n;
@@ -178,9 +183,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
       const int64_t lp = (wg_base + (int64_t)wave * 64) / CSA2_BLOCK + 4 * lane;
       if (lane < a.iters && lp * CSA2_BLOCK < n) pv = (int)page_of(a.g, b, lp);
     }
+    constexpr bool kLdsKeys = LDSK;
+    constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
     struct Chunk {
-      u32x4_t kc[kGroups];
-      uint32_t ks[kGroups];
+      u32x4_t kc[kLdsKeys ? kGroups + 1 : kGroups];
+      uint32_t ks[kLdsKeys ? 1 : kGroups];
     };
     auto issue = [&](Chunk& ck, int lb) {
       __amdgpu_buffer_rsrc_t r = rs;
@@ -193,12 +200,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
                                               (short)0, cnt * CSA2_IDX_BYTES, kRsrcWord3);
         so = 0;
       }
+      if constexpr (kLdsKeys) {
+        // The chunk's 64 x 68 bytes in order: lane l takes bytes 16l + 1024q (q < 4) and
+        // 4096 + 16(l mod 16).
 #pragma unroll
-      for (int gi = 0; gi < kGroups; ++gi) {
-        ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(r, voff_c + gi * 16 * CSA2_IDX_BYTES, so, 0);
-        ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(r, voff_s + gi * 16 * CSA2_IDX_BYTES, so, 0);
+        for (int q = 0; q < kGroups; ++q)
+          ck.kc[q] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane + 1024 * q, so, kNonTemporal);
+        ck.kc[kGroups] = __builtin_amdgcn_raw_buffer_load_b128(r, 4096 + 16 * (lane & 15), so, kNonTemporal);
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+          ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(r, voff_c + gi * 16 * CSA2_IDX_BYTES, so, 0);
+          ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(r, voff_s + gi * 16 * CSA2_IDX_BYTES, so, 0);
+        }
       }
     };
+    __shared__ __align__(16) uint32_t kstage[kLdsKeys ? kWaves : 1][kLdsKeys ? 64 * CSA2_IDX_BYTES / 4 : 4];
     bf16x8_t qa[MAXPAIRS][4];
     float wv[MAXPAIRS][4];
     const int nrows = r1 - r0;
@@ -212,12 +229,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     __shared__ __align__(16) float sbuf[kWgStage ? 1 : kWaves][2 * MAXPAIRS][64];
     float (*sb)[64] = sbuf[kWgStage ? 0 : wave];
     auto consume = [&](const Chunk& ck, int lb) {
+      u32x4_t kcv[kGroups];
+      uint32_t ksv[kGroups];
+      if constexpr (kLdsKeys) {
+        // Through the wave's LDS stage: lane (m, g) of group gi takes entry 16gi + m's
+        // bytes 16g .. 16g+15 and its scale byte g (the layout the direct loads give).
+        uint32_t* kst = kstage[wave];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) *reinterpret_cast<u32x4_t*>(kst + 4 * lane + 256 * q) = ck.kc[q];
+        if (lane < 16) *reinterpret_cast<u32x4_t*>(kst + 1024 + 4 * lane) = ck.kc[kGroups];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+          const uint32_t* w = kst + (16 * gi + m) * (CSA2_IDX_BYTES / 4);
+          kcv[gi] = u32x4_t{w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]};
+          ksv[gi] = (w[16] >> (8 * g)) & 0xFFu;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+          kcv[gi] = ck.kc[gi];
+          ksv[gi] = ck.ks[gi];
+        }
+      }
 #pragma unroll
       for (int gi = 0; gi < kGroups; ++gi) {
-        const float sc = e8m0_operand(ck.ks[gi]);
+        const float sc = e8m0_operand(ksv[gi]);
         bf16x8_t kb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kb[c] = fp4x8_to_bf16(ck.kc[gi][c], sc);
+        for (int c = 0; c < 4; ++c) kb[c] = fp4x8_to_bf16(kcv[gi][c], sc);
 #pragma unroll
         for (int p = 0; p < MAXPAIRS; ++p) {
           if (p < npairs) {
@@ -379,6 +422,16 @@ __global__ __launch_bounds__(64) void k_scan_kept(ScanArgs a) {
 
 template <int PARTS, bool PAGED>
 static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
+  // Contiguous key reads (LDSK) where they measured faster: both parts in one launch,
+  // long workgroups, one row pair per request, contiguous pools (the 64 x 128K decode
+  // step 117.7 -> 115.0 us, 1M-context 105.7 -> 101.7 us; the entry-only scan and short
+  // workgroups were 1 us slower with them).
+  if constexpr (PARTS == 3 && !PAGED) {
+    if (max_rows_per_req <= 2 && a.iters >= kMaxIters) {
+      k_scan<1, PARTS, PAGED, true><<<grid, dim3(256), 0, st>>>(a);
+      return;
+    }
+  }
   if (max_rows_per_req <= 2)
     k_scan<1, PARTS, PAGED><<<grid, dim3(256), 0, st>>>(a);
   else if (max_rows_per_req <= 4)
