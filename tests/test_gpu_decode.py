@@ -171,6 +171,29 @@ def test_request_without_summaries_in_the_pool(csa2):
     assert np.isfinite(got["out"][3]).all() and np.isfinite(got["lse"][3]).all()
 
 
+def test_contiguous_key_reads_with_ragged_tails(csa2):
+    # Eight one-row requests, long enough (ceil(max_entries / 256) x 8 >= 8,192 tiles) that
+    # the decode's one scan launch runs 4 chunks per wave, where each wave reads its
+    # 64-entry chunk of keys as one contiguous run and regroups it through LDS.  The
+    # lengths leave partial chunks and workgroups at every request's end.  The decode's
+    # scores equal the entry-only scan's (direct loads) bit for bit, and rows are judged
+    # against the oracle.
+    lens = [262144 + 37, 262144 - 1, 200003, 131072 + 64 * 5 + 1, 70001, 4097, 65, 262144 - 200]
+    tiles1, iters = -(-max(lens) // 256), 1
+    while iters < 4 and tiles1 * len(lens) >= 2048 * 2 * iters:
+        iters *= 2
+    assert iters == 4
+    wl = make_workload("ldsk", 52, lens, rows_per_req=1, n_needles=8)
+    _log(f"contiguous key reads, ragged lengths {lens}")
+    got = run_decode(csa2, wl)
+    dw = upload(wl)
+    ref = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
+    for r, n in enumerate(lens):
+        assert np.array_equal(got["scores"][r, :n].view(np.uint32), ref[r, :n].view(np.uint32)), f"row {r}"
+    rows = [0, 3, 6]
+    judge(wl, got, oracle.decode(wl, rows=rows), rows=rows)
+
+
 def test_bench_scale_batches_on_sampled_rows(csa2):
     # The two 285 MB batches bench.py times the scan on (64 x 65,536 entries, 4 chunks per
     # wave; 4 x 1,048,576 entries), in the launch configuration it times: the full-scan
