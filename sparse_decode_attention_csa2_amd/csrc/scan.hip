@@ -167,7 +167,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     // entries: a lane's offset is fixed, the chunk offset is scalar and the group offset
     // immediate, and reads past the request's end return zeros (never stored).
     // Chunks of loads in flight per wave (fewer with more query rows held in registers).
-    constexpr int kDepth = MAXPAIRS <= 2 ? CSA2_SCAN_DEPTH : (MAXPAIRS == 4 ? 2 : 1);
+    // The contiguous path (LDSK) keeps two: with three its regroup runs slower (64 x 128K
+    // decode step 114.8 -> 112.0 us, 1M-context 101.4 -> 98.2 us with two).
+    constexpr int kDepth = LDSK ? 2 : (MAXPAIRS <= 2 ? CSA2_SCAN_DEPTH : (MAXPAIRS == 4 ? 2 : 1));
     const int iters = a.iters;
     const int64_t wg_base = (int64_t)(blockIdx.x - a.block_tiles) * (kWaves * 64) * iters;
     if (wg_base >= n) return;   // uniform over the workgroup
@@ -424,8 +426,8 @@ template <int PARTS, bool PAGED>
 static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
   // Contiguous key reads (LDSK) where they measured faster: both parts in one launch,
   // long workgroups, one row pair per request, contiguous pools (the 64 x 128K decode
-  // step 117.7 -> 115.0 us, 1M-context 105.7 -> 101.7 us; the entry-only scan and short
-  // workgroups were 1 us slower with them).
+  // step 117.7 -> 112.0 us, 1M-context 105.7 -> 98.2 us; short workgroups were slower
+  // with them and the entry-only scan no faster).
   if constexpr (PARTS == 3 && !PAGED) {
     if (max_rows_per_req <= 2 && a.iters >= kMaxIters) {
       k_scan<1, PARTS, PAGED, true><<<grid, dim3(256), 0, st>>>(a);
