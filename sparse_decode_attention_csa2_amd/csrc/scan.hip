@@ -35,6 +35,9 @@ typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
 #define CSA2_SCAN_WG_STAGE 1
 #endif
 constexpr int kMaxIters = CSA2_SCAN_MAX_ITERS;      // chunks per wave, at most
+// Entry-only scans on the contiguous-read path go to 8 chunks per wave (50.7-50.8 us on
+// the 64 x 65,536-entry scan against 51.6 at 4).
+constexpr int kMaxItersLdsk = 8;
 constexpr int kWgRows = 4;                          // rows staged per workgroup
 #ifndef CSA2_SCAN_WAVES_PER_EU
 #define CSA2_SCAN_WAVES_PER_EU 4
@@ -167,9 +170,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     // entries: a lane's offset is fixed, the chunk offset is scalar and the group offset
     // immediate, and reads past the request's end return zeros (never stored).
     // Chunks of loads in flight per wave (fewer with more query rows held in registers).
-    // The contiguous path (LDSK) keeps two: with three its regroup runs slower (64 x 128K
-    // decode step 114.8 -> 112.0 us, 1M-context 101.4 -> 98.2 us with two).
-    constexpr int kDepth = LDSK ? 2 : (MAXPAIRS <= 2 ? CSA2_SCAN_DEPTH : (MAXPAIRS == 4 ? 2 : 1));
+    // The contiguous path (LDSK) keeps one, which leaves registers for five waves per
+    // SIMD (64 x 65,536-entry scan 51.6 us with one, 54.0-54.5 with two, 56.6-57.8 with
+    // three; decode steps also fastest with one).
+    constexpr int kDepth = LDSK ? 1 : (MAXPAIRS <= 2 ? CSA2_SCAN_DEPTH : (MAXPAIRS == 4 ? 2 : 1));
     const int iters = a.iters;
     const int64_t wg_base = (int64_t)(blockIdx.x - a.block_tiles) * (kWaves * 64) * iters;
     if (wg_base >= n) return;   // uniform over the workgroup
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     // workgroup); with more rows each wave flushes every chunk.
     constexpr bool kWgStage = CSA2_SCAN_WG_STAGE && 2 * MAXPAIRS <= kWgRows;
     constexpr int kStageRows = kWgStage ? 2 * MAXPAIRS : 1;
-    constexpr int kStageLen = kWgStage ? kWaves * 64 * kMaxIters : 1;
+    constexpr int kStageLen = kWgStage ? kWaves * 64 * (LDSK && PARTS == 1 ? kMaxItersLdsk : kMaxIters) : 1;
     __shared__ __align__(16) float wstage[kStageRows][kStageLen];
     __shared__ __align__(16) float sbuf[kWgStage ? 1 : kWaves][2 * MAXPAIRS][64];
     float (*sb)[64] = sbuf[kWgStage ? 0 : wave];
@@ -424,11 +428,11 @@ __global__ __launch_bounds__(64) void k_scan_kept(ScanArgs a) {
 
 template <int PARTS, bool PAGED>
 static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
-  // Contiguous key reads (LDSK) where they measured faster: both parts in one launch,
-  // long workgroups, one row pair per request, contiguous pools (the 64 x 128K decode
-  // step 117.7 -> 112.0 us, 1M-context 105.7 -> 98.2 us; short workgroups were slower
-  // with them and the entry-only scan no faster).
-  if constexpr (PARTS == 3 && !PAGED) {
+  // Contiguous key reads (LDSK) where they measured faster: long workgroups, one row
+  // pair per request, contiguous pools (64 x 65,536-entry scan 54.9 -> 50.8 us; decode
+  // steps 117.7 -> 110.9 us at 64 x 128K, 105.7 -> 97.7 us at 1M context; short
+  // workgroups were slower with them).
+  if constexpr ((PARTS == 3 || PARTS == 1) && !PAGED) {
     if (max_rows_per_req <= 2 && a.iters >= kMaxIters) {
       k_scan<1, PARTS, PAGED, true><<<grid, dim3(256), 0, st>>>(a);
       return;
@@ -464,6 +468,10 @@ hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool bloc
   const int64_t tiles1 = (a.g.max_entries + kTile - 1) / kTile;
   int iters = 1;
   while (iters < kMaxIters && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
+  // Entry-only scans that take the contiguous-read path (see launch_scan_rows) keep
+  // doubling up to kMaxItersLdsk.
+  if (entries && !blocks && !a.g.page_table && max_rows_per_req <= 2 && iters >= kMaxIters)
+    while (iters < kMaxItersLdsk && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
   a.iters = iters;
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;
   a.blk_groups = iters < kGroups ? iters : kGroups;

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle import parity
-from synth import make_config, make_workload
+from synth import to_paged, make_config, make_workload
 from synth.device import upload
 
 pytestmark = pytest.mark.gpu
@@ -176,8 +176,10 @@ def test_contiguous_key_reads_with_ragged_tails(csa2):
     # the decode's one scan launch runs 4 chunks per wave, where each wave reads its
     # 64-entry chunk of keys as one contiguous run and regroups it through LDS.  The
     # lengths leave partial chunks and workgroups at every request's end.  The decode's
-    # scores equal the entry-only scan's (direct loads) bit for bit, and rows are judged
-    # against the oracle.
+    # scores and the entry-only scan's equal a direct-load scan's bit for bit, and rows are judged
+    # against the oracle.  The entry-only scan of these contiguous pools takes the
+    # contiguous reads too, so the direct-load reference is the scan over the same
+    # workload in paged pools (bit-exact with contiguous ones).
     lens = [262144 + 37, 262144 - 1, 200003, 131072 + 64 * 5 + 1, 70001, 4097, 65, 262144 - 200]
     tiles1, iters = -(-max(lens) // 256), 1
     while iters < 4 and tiles1 * len(lens) >= 2048 * 2 * iters:
@@ -187,9 +189,12 @@ def test_contiguous_key_reads_with_ragged_tails(csa2):
     _log(f"contiguous key reads, ragged lengths {lens}")
     got = run_decode(csa2, wl)
     dw = upload(wl)
-    ref = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
+    flat = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
+    pw = upload(to_paged(wl))
+    ref = csa2.index_score(pw.rg, pw.idx_k, pw.q_idx, pw.w).cpu().numpy()
     for r, n in enumerate(lens):
         assert np.array_equal(got["scores"][r, :n].view(np.uint32), ref[r, :n].view(np.uint32)), f"row {r}"
+        assert np.array_equal(flat[r, :n].view(np.uint32), ref[r, :n].view(np.uint32)), f"row {r}"
     rows = [0, 3, 6]
     judge(wl, got, oracle.decode(wl, rows=rows), rows=rows)
 
