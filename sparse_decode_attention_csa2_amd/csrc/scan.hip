@@ -167,8 +167,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     // wave keeps kDepth chunks of loads in flight (a ring in registers): a chunk's slot
     // is refilled with the loads of the chunk kDepth steps ahead as soon as it has been
     // converted.  Keys are read through a buffer descriptor over the workgroup's
-    // entries: a lane's offset is fixed, the chunk offset is scalar and the group offset
-    // immediate, and reads past the request's end return zeros (never stored).
+    // entries (per-lane offset = the lane's offset plus the chunk's, group offset
+    // immediate); reads past the request's end return zeros (never stored).
     // Chunks of loads in flight per wave (fewer with more query rows held in registers).
     // The contiguous path (LDSK) keeps one, which leaves registers for five waves per
     // SIMD (64 x 65,536-entry scan 51.6 us with one, 54.0-54.5 with two, 56.6-57.8 with
@@ -195,29 +195,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
       u32x4_t kc[kLdsKeys ? kGroups + 1 : kGroups];
       uint32_t ks[kLdsKeys ? 1 : kGroups];
     };
+    // The chunk offset goes into the per-lane offset (the scalar offset stays 0), so the
+    // descriptor's range check, which covers the per-lane and instruction offsets,
+    // bounds every read by the workgroup's (or, paged, the page's) entries.
     auto issue = [&](Chunk& ck, int lb) {
       __amdgpu_buffer_rsrc_t r = rs;
-      int so = lb * CSA2_IDX_BYTES;
+      int co = lb * CSA2_IDX_BYTES;
       if constexpr (PAGED) {
         const int c = (lb - wave * 64) / (kWaves * 64);   // the wave's chunk index (uniform)
         const int64_t page = __builtin_amdgcn_readlane(pv, c);
         const int cnt = min(64, wg_n - lb);
         r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.idx_k + page * (CSA2_BLOCK * CSA2_IDX_BYTES)),
                                               (short)0, cnt * CSA2_IDX_BYTES, kRsrcWord3);
-        so = 0;
+        co = 0;
       }
       if constexpr (kLdsKeys) {
         // The chunk's 64 x 68 bytes in order: lane l takes bytes 16l + 1024q (q < 4) and
         // 4096 + 16(l mod 16).
+        const int vo = co + 16 * lane;
 #pragma unroll
         for (int q = 0; q < kGroups; ++q)
-          ck.kc[q] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane + 1024 * q, so, kNonTemporal);
-        ck.kc[kGroups] = __builtin_amdgcn_raw_buffer_load_b128(r, 4096 + 16 * (lane & 15), so, kNonTemporal);
+          ck.kc[q] = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 1024 * q, 0, kNonTemporal);
+        ck.kc[kGroups] = __builtin_amdgcn_raw_buffer_load_b128(r, co + 4096 + 16 * (lane & 15), 0, kNonTemporal);
       } else {
+        const int vc = co + voff_c, vs = co + voff_s;
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi) {
-          ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(r, voff_c + gi * 16 * CSA2_IDX_BYTES, so, 0);
-          ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(r, voff_s + gi * 16 * CSA2_IDX_BYTES, so, 0);
+          ck.kc[gi] = __builtin_amdgcn_raw_buffer_load_b128(r, vc + gi * 16 * CSA2_IDX_BYTES, 0, 0);
+          ck.ks[gi] = __builtin_amdgcn_raw_buffer_load_b8(r, vs + gi * 16 * CSA2_IDX_BYTES, 0, 0);
         }
       }
     };

@@ -425,8 +425,12 @@ __device__ void coarse_cand(const SelectArgs& a, int r, int nb, SelShared& sh, u
     if (kout) kout[pos] = blk;
     if (blk == nb - 1) sh.flag = 1;
   };
-  gather(items, [&](int i) { return i % K < cn[i / K]; }, [&](int i, bool ok) { return cs[ok ? i : 0]; }, kbuf,
-         sh);
+  // gather() evaluates valid(i) for every i of its last whole batch (up to NT * kGB - 1,
+  // past `items`), so the slice index is clamped to the row's slices: cand_n is the
+  // last buffer of the decode workspace and must not be read past its end.
+  const int last_slice = a.n_slices - 1;
+  gather(items, [&](int i) { return i % K < cn[min(i / K, last_slice)]; },
+         [&](int i, bool ok) { return cs[ok ? i : 0]; }, kbuf, sh);
   __syncthreads();
   int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), K, sh, emit);
   __syncthreads();

@@ -225,3 +225,93 @@ def test_bench_scale_batches_on_sampled_rows(csa2):
         ref = oracle.request_scores(w4, b)[0]
         err = np.abs(s4[b, :w4.n_entries(b)] - ref).max() / np.abs(ref).mean()
         assert err <= 1e-5, f"1M request {b}: score error {err:.3g}"
+
+
+@pytest.mark.parametrize("n_keep", [1, 4])
+def test_sliced_coarse_stage_with_few_kept_blocks(csa2, n_keep):
+    # Rows with more than 4,096 blocks rank 1,024-block slices first and then the slices'
+    # candidates (n_slices x n_keep of them).  With n_keep 1 or 4 those candidates are far
+    # fewer than one gather batch of the select, whose validity check then runs over
+    # slots past the last slice's count.  Kept blocks equal the one-level block filter's
+    # and rows are judged against the oracle.
+    lens = [64 * 5000 + 17, 64 * 4500 + 3]
+    wl = make_workload("sliced", 61 + n_keep, lens, rows_per_req=1, n_needles=8)
+    _log(f"sliced coarse stage, n_keep {n_keep}, lengths {lens}")
+    got = run_decode(csa2, wl, n_keep=n_keep)
+    judge(wl, got, oracle.decode(wl, n_keep=n_keep), n_keep=n_keep)
+    dw = upload(wl)
+    kept, n_kept, _ = csa2.block_filter(dw.rg, dw.blk_sum, dw.q_idx, dw.w, n_keep=n_keep)
+    assert np.array_equal(kept.cpu().numpy(), got["kept"]) and np.array_equal(n_kept.cpu().numpy(), got["n_kept"])
+
+
+def test_decode_with_workspace_at_the_end_of_an_allocation(csa2):
+    # The workspace is exactly csa2_decode_workspace_size bytes and ends where its
+    # allocation ends (a 2 MiB multiple, which the caching allocator hands out whole);
+    # its last buffer holds the sliced coarse stage's per-slice counts.
+    wl = make_workload("exactws", 71, [64 * 5000 + 17], rows_per_req=1, n_needles=8)
+    dw = upload(wl)
+    d = csa2.Decoder(*dw.decode_inputs(), k=wl.k, n_keep=1, sm_scale=wl.sm_scale)
+    n = d.ws_bytes
+    total = -(-n // (2 << 20)) * (2 << 20)
+    big = torch.empty((total,), dtype=torch.uint8, device="cuda")
+    d.ws = big[total - n:]
+    assert d.ws.data_ptr() % 256 == 0 and d.ws.numel() == n
+    _log(f"decode with a {n}-byte workspace at the end of a {total}-byte allocation")
+    d.run()
+    torch.cuda.synchronize()
+    got = dict(out=d.out.cpu().numpy(), lse=d.lse.cpu().numpy(), sel=d.sel_idx.cpu().numpy(),
+               n_sel=d.n_sel.cpu().numpy(), kept=d.kept.cpu().numpy(), n_kept=d.n_kept.cpu().numpy())
+    judge(wl, got, oracle.decode(wl, n_keep=1), n_keep=1)
+
+
+def test_entry_scan_eight_chunks_per_wave_ragged(csa2):
+    # The entry-only scan over contiguous pools runs 8 chunks per wave (2,048-entry
+    # workgroups) once ceil(max_entries / 256) x B >= 16,384.  Lengths that are not
+    # multiples of 2,048 or 64 leave partial workgroups and chunks at every request's end.
+    # Scores equal the direct-load scan's (the same workload over paged pools) bit for
+    # bit, and sampled requests are judged against the oracle.
+    lens = [524288 + 37, 524288 - 1, 400003, 262144 + 64 * 5 + 1, 140001, 4097, 65, 524288 - 200]
+    tiles1, iters = -(-max(lens) // 256), 1
+    while iters < 8 and tiles1 * len(lens) >= 2048 * 2 * iters:
+        iters *= 2
+    assert iters == 8
+    wl = make_workload("ldsk8", 53, lens, rows_per_req=1, n_needles=8, scan_only=True)
+    _log(f"entry-only scan at 8 chunks per wave, ragged lengths {lens}")
+    dw = upload(wl)
+    flat = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
+    del dw
+    pw = upload(to_paged(wl))
+    ref = csa2.index_score(pw.rg, pw.idx_k, pw.q_idx, pw.w).cpu().numpy()
+    del pw
+    torch.cuda.empty_cache()
+    for r, n in enumerate(lens):
+        assert np.array_equal(flat[r, :n].view(np.uint32), ref[r, :n].view(np.uint32)), f"row {r}"
+    for b in (2, 6, 7):
+        want = oracle.request_scores(wl, b)[0]
+        err = np.abs(flat[b, :lens[b]] - want).max() / np.abs(want).mean()
+        assert err <= 1e-5, f"request {b}: score error {err:.3g}"
+
+
+def test_decode_bits_do_not_depend_on_the_grid(csa2):
+    # Same inputs, different workgroup counts: a larger host-side max_entries (still within
+    # the pools) changes the scan's workgroup size and count and the select's gather range;
+    # every output stays identical bit for bit.
+    wl = make_config(2)
+    dw = upload(wl)
+    outs = []
+    for scale in (1, 4):
+        rg = dw.rg
+        big = type(rg)(**{f: getattr(rg, f) for f in rg.__dataclass_fields__})
+        big.max_entries = min(rg.total_entries, rg.max_entries * scale)
+        d = csa2.Decoder(big, *dw.decode_inputs()[1:], k=wl.k, n_keep=wl.n_keep, sm_scale=wl.sm_scale)
+        d.run()
+        torch.cuda.synchronize()
+        _log(f"max_entries {big.max_entries}: workspace {d.ws_bytes} bytes")
+        outs.append({k: getattr(d, k).cpu().numpy() for k in ("out", "lse", "sel_idx", "n_sel", "kept", "n_kept")})
+        sc = d.scores.cpu().numpy()
+        outs[-1]["scores"] = np.concatenate([sc[r, :wl.n_entries(int(wl.row_req[r]))] for r in range(wl.num_rows)])
+    for key in outs[0]:
+        a, b = outs[0][key], outs[1][key]
+        if a.dtype == np.float32:
+            a, b = a.view(np.uint32), b.view(np.uint32)
+        assert np.array_equal(a, b), key
