@@ -461,6 +461,43 @@ def test_mx_attention_closed_forms_and_bound():
     assert np.abs(o1 - o0).max() > 0        # P really is rounded
 
 
+def test_mx_attention_rounds_p_in_blocks_of_keys():
+    # The expected output is built head by head and key block by key block (32
+    # consecutive keys, a partial last block of 8) with the independent rounding above:
+    # q rounded per head in blocks of 32 dims, the weight on each key's codes
+    # w_i = p_i * scale_i rounded per head in blocks of keys, normaliser and lse from the
+    # unrounded p.  Rounding the weights along heads instead (blocks of 32 heads per key)
+    # gives a clearly different output on the same data.
+    rng = np.random.default_rng(13)
+    n, H, sm = 40, 64, 0.07
+    codes = oracle.E2M1[rng.integers(0, 16, size=(n, 512))]
+    scales = np.ones(n)
+    scales[-8:] = rng.uniform(0.01, 0.1, 8)          # the last keys act as scaled window tokens
+    q = rng.standard_normal((H, 512)) * 0.5
+    blocks = [(0, 32), (32, 40)]
+    qm = np.stack([np.concatenate([_mx_reference(q[h, 32 * j:32 * j + 32]) for j in range(16)]) for h in range(H)])
+    want = np.zeros((H, 512))
+    want_lse = np.zeros(H)
+    w_all = np.zeros((H, n))
+    l_all = np.zeros(H)
+    for h in range(H):
+        z = np.array([sm * scales[i] * float(qm[h] @ codes[i]) for i in range(n)])
+        mz = z.max()
+        p = np.exp(z - mz)
+        w = p * scales
+        w_all[h], l_all[h] = w, p.sum()
+        wr = np.concatenate([_mx_reference(w[a:b]) for a, b in blocks])
+        want[h] = (wr[:, None] * codes).sum(axis=0) / p.sum()
+        want_lse[h] = mz + np.log(p.sum())
+    out, lse = oracle.joint_attention_mx(q, codes, scales, sm)
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, want_lse, rtol=0, atol=1e-12)
+    by_heads = np.stack([np.concatenate([_mx_reference(w_all[a:b, i]) for a, b in ((0, 32), (32, 64))])
+                         for i in range(n)], axis=1)
+    other = (by_heads @ codes) / l_all[:, None]
+    assert np.abs(other - want).max() > 1e-3 * np.abs(want).max()
+
+
 # ---------------------------------------------------------------------------------
 # Cache write.
 # ---------------------------------------------------------------------------------
@@ -550,3 +587,44 @@ def test_cache_write_is_scale_invariant():
         row = int(oracle.entry_rows(wl, bb, np.array([t]))[0])
         assert np.array_equal(c["main_kv"][row, :256], a["main_kv"][row, :256])
         assert np.array_equal(c["main_kv"][row, 256:].astype(int), a["main_kv"][row, 256:].astype(int) + 1)
+
+
+def test_rms_norm_closed_forms():
+    # y = x * gamma / sqrt(mean(x^2) + eps), per row.  A sum in place of the mean, eps
+    # outside the square root, or gamma applied as a scalar each fail one of these.
+    assert np.allclose(oracle.rms_norm(np.array([[3.0, 4.0]]), np.ones(2), 0.0),
+                       [[3 * math.sqrt(2) / 5, 4 * math.sqrt(2) / 5]], rtol=0, atol=1e-15)
+    assert np.allclose(oracle.rms_norm(np.ones((1, 4)), np.ones(4), 3.0), 0.5, rtol=0, atol=1e-15)
+    assert np.allclose(oracle.rms_norm(np.array([[2.0, 2.0]]), np.array([1.0, 3.0]), 0.0), [[1.0, 3.0]],
+                       rtol=0, atol=1e-15)
+    assert np.allclose(oracle.rms_norm(np.array([[1.0, 1.0], [-2.0, 2.0]]), np.ones(2), 0.0),
+                       [[1.0, 1.0], [-1.0, 1.0]], rtol=0, atol=1e-15)
+    # eps dominates a tiny vector: y = x / sqrt(eps)
+    assert np.allclose(oracle.rms_norm(np.full((1, 8), 1e-9), np.ones(8), 1e-2), 1e-8, rtol=1e-9, atol=0)
+
+
+def test_cache_write_golden_record():
+    # A token pair with distinct partner and own vectors, its main and index records and
+    # block summary derived by hand (tests/golden/cache_write_record.json).  Pooling that
+    # ignored the partner, RMSNorm over a sum, or a wrong code/scale rule all change them.
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "cache_write_record.json")))
+
+    def bf16_vec(nonzero, dim):
+        v = np.zeros(dim, dtype=np.float32)
+        for k, x in nonzero.items():
+            v[int(k)] = x
+        return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[None]
+
+    wl = make_workload("golden", 5, [1], rows_per_req=1, n_needles=0)
+    res = oracle.cache_write(wl, np.array([1]), bf16_vec(g["kv_tok_nonzero"], 512),
+                             bf16_vec(g["idx_tok_nonzero"], 128), bf16_vec(g["ring_kv_nonzero"], 512),
+                             bf16_vec(g["ring_idx_nonzero"], 128), np.ones(512), np.ones(128), eps=g["eps"])
+    for pool, key, width in (("main_kv", "main_expected", 288), ("idx_k", "index_expected", 68),
+                             ("blk_sum", "summary_expected", 128)):
+        want = np.zeros(width, dtype=np.int64)
+        for k, v in g[key].items():
+            want[int(k)] = v
+        assert np.array_equal(res[pool][0].astype(np.int64), want), pool
+    assert sorted(res["written"]) == [(0, 0)]
