@@ -35,8 +35,9 @@
  *     csa2_ragged / csa2_decode_args structs themselves are host memory, read during the
  *     call only.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call
- *     synchronises, allocates device memory or keeps state between calls, so calls on
- *     different streams with distinct outputs and workspaces may run concurrently.
+ *     synchronises, allocates device memory or keeps state between calls (except the
+ *     static workspace of csa2_decode_static), so calls on different streams with
+ *     distinct outputs and workspaces may run concurrently.
  *   - Return value: CSA2_OK (0) or a positive CSA2_ERR_* code.  Argument checks happen on
  *     the host before anything is launched; a failed check launches nothing.  A launch
  *     failure returns CSA2_ERR_HIP.  csa2_last_error() gives a message for the calling
@@ -233,6 +234,22 @@ typedef struct csa2_decode_args {
 
 int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_decode_workspace_size(const csa2_decode_args* a);
+
+/*
+ * csa2_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same launch chain
+ * as csa2_decode, with its workspace in a static device buffer of CSA2_STATIC_WS_BYTES
+ * that the library holds on every device it runs on until the process ends.  The caller
+ * passes inputs and outputs as for csa2_decode; the call allocates nothing.  Returns
+ * CSA2_ERR_WORKSPACE_TOO_SMALL (nothing launched) when csa2_decode_workspace_size(a)
+ * exceeds CSA2_STATIC_WS_BYTES.  Every call on one device shares that device's buffer:
+ * calls that overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller.  `stream` must belong to the current device.  No part of
+ * the buffer needs to start at zero: every value the kernels read there is written
+ * earlier in the same call.
+ */
+#define CSA2_STATIC_WS_BYTES ((size_t)64 << 20)
+int csa2_decode_static(const csa2_decode_args* a, void* stream);
 
 /*
  * Cache write (the step before the path; SGLang blog, section "Small-operator fusion and

@@ -26,6 +26,7 @@ QP_BF16, QP_MXFP8 = 0, 1
 DECODE_EVENTS = 5
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = 0, 1, 2, 3, 4
+STATIC_WS_BYTES = 64 << 20
 
 
 class Csa2Error(RuntimeError):
@@ -63,7 +64,7 @@ class _DecodeArgs(ctypes.Structure):
 
 
 EXPORTS = ("csa2_index_score", "csa2_block_filter", "csa2_topk", "csa2_sparse_attn", "csa2_cache_write",
-           "csa2_sparse_attn_workspace_size", "csa2_decode", "csa2_decode_workspace_size",
+           "csa2_sparse_attn_workspace_size", "csa2_decode", "csa2_decode_workspace_size", "csa2_decode_static",
            "csa2_debug_dequant", "csa2_debug_mxfp8", "csa2_debug_stream_read", "csa2_status_string", "csa2_last_error",
            "csa2_version")
 
@@ -89,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "csa2_sparse_attn_workspace_size": ([RG, I32], SZ),
         "csa2_decode": ([DA, P, SZ, P], ctypes.c_int),
         "csa2_decode_workspace_size": ([DA], SZ),
+        "csa2_decode_static": ([DA, P], ctypes.c_int),
         "csa2_debug_dequant": ([I32, P, P, I64, P, P], ctypes.c_int),
         "csa2_debug_stream_read": ([P, I64, P, P], ctypes.c_int),
         "csa2_debug_mxfp8": ([P, I64, P, P], ctypes.c_int),
@@ -320,6 +322,14 @@ class Decoder:
         self._args.events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
         _check(self._lib.csa2_decode(ctypes.byref(self._args), _ptr(self.ws), self.ws_bytes,
                                      _stream() if stream is None else stream))
+
+
+    def run_static(self, stream: int | None = None) -> None:
+        """Enqueue one decode step through csa2_decode_static: the library's static
+        per-device workspace instead of ``self.ws`` (no allocation; calls on one device
+        share that workspace and must not overlap)."""
+        self._args.events = None
+        _check(self._lib.csa2_decode_static(ctypes.byref(self._args), _stream() if stream is None else stream))
 
 
 def capture_calls(fns) -> "torch.cuda.CUDAGraph":

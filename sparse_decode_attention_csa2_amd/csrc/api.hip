@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "csa2_internal.h"
 
 using namespace csa2;
@@ -143,6 +145,39 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int kind, const uint8_t* 
   }
   const int dim = (kind == CSA2_DQ_IDX) ? CSA2_IDX_D : CSA2_D;
   for (int j = 0; j < 8; ++j) out[i * dim + 8 * grp + j] = v[j];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------
+// Static workspace of csa2_decode_static: one buffer per device, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (in host code the name
+// stands for a host-side shadow, not device memory): the buffer's device address is
+// looked up once per device, with that device current, and only that address is used.
+// ---------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[CSA2_STATIC_WS_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_workspace(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA2_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(CSA2_ERR_HIP, "static workspace has no valid device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CSA2_OK;
 }
 
 }  // namespace
@@ -553,6 +588,18 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   LAUNCH(launch_attn_merge(at, st), "attention merge");
   LAUNCH(mark(4), "event record");
   return CSA2_OK;
+}
+
+int csa2_decode_static(const csa2_decode_args* a, void* stream) {
+  if (!a) return fail(CSA2_ERR_INVALID_ARG, "args is NULL");
+  const size_t need = csa2_decode_workspace_size(a);
+  if (need > CSA2_STATIC_WS_BYTES)
+    return fail(CSA2_ERR_WORKSPACE_TOO_SMALL,
+                "decode needs %zu workspace bytes; the static workspace holds %zu (CSA2_STATIC_WS_BYTES)", need,
+                (size_t)CSA2_STATIC_WS_BYTES);
+  void* ws = nullptr;
+  CHECK(static_workspace(&ws));
+  return csa2_decode(a, ws, CSA2_STATIC_WS_BYTES, stream);
 }
 
 int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales, int64_t n, float* out,
