@@ -275,6 +275,10 @@ int csa2_decode_static(const csa2_decode_args* a, void* stream);
  * fields of rg are ignored; N_b = entry_off[b+1] - entry_off[b] already counts the new
  * entries.  gamma_kv [512] / gamma_idx [128] fp32; eps > 0.  The ring slots are read
  * before any is written.  Rows whose position is negative are skipped.
+ * RoPE: the same section lists a rotary embedding in the fused chain; it is not applied
+ * here.  Attention in this library uses K = V = the whole 512-dim latent with no rotary
+ * part (no separate RoPE dims are stored in the 288-B entry), so the write has nothing
+ * to rotate; a caller whose latent carries rotary dims applies RoPE to kv_tok first.
  */
 int csa2_cache_write(const csa2_ragged* rg, const int64_t* row_pos, const uint16_t* kv_tok, const uint16_t* idx_tok,
                      uint16_t* ring_kv, uint16_t* ring_idx, const float* gamma_kv, const float* gamma_idx, float eps,

@@ -12,6 +12,8 @@
 // operand holds two query rows (8 heads each), so the rows of one request (verify
 // rows) share a single read of its keys.  The ReLU and the head weights are applied to
 // the fp32 MFMA output and the two half-sums meet with one cross-lane add.
+#include <type_traits>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -42,6 +44,17 @@ constexpr int kWgRows = 4;                          // rows staged per workgroup
 #ifndef CSA2_SCAN_WAVES_PER_EU
 #define CSA2_SCAN_WAVES_PER_EU 4
 #endif
+#ifndef CSA2_SCAN_LDSK_WAVES
+#define CSA2_SCAN_LDSK_WAVES CSA2_SCAN_WAVES_PER_EU
+#endif
+
+// Waits until at most N vector-memory operations of this wave are outstanding (s_waitcnt
+// with the other counters left alone).  The compiler sees the wait and counts on it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int MAXPAIRS>
 __device__ __forceinline__ void load_query(const ScanArgs& a, int r0, int r1, bf16x8_t (&qa)[MAXPAIRS][4],
@@ -147,7 +160,8 @@ __device__ __forceinline__ void flush_chunk(float (*sb)[64], int nrows, int r0, 
 // apart plus scale bytes, partial lines that the L2 completes across loads, which the
 // non-temporal hint defeats).
 template <int MAXPAIRS, int PARTS, bool PAGED, bool LDSK = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS == 1 ? CSA2_SCAN_WAVES_PER_EU : (MAXPAIRS == 8 ? 1 : 2)))) void k_scan(ScanArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    LDSK ? CSA2_SCAN_LDSK_WAVES : (MAXPAIRS == 1 ? CSA2_SCAN_WAVES_PER_EU : (MAXPAIRS == 8 ? 1 : 2))))) void k_scan(ScanArgs a) {
   const int b = blockIdx.y;
   int64_t e0, n;
   req_entries(a.g, b, e0, n, PAGED);
@@ -191,6 +205,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
     }
     constexpr bool kLdsKeys = LDSK;
     constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
+    constexpr int kChunkLoads = kLdsKeys ? kGroups + 1 : 2 * kGroups;   // load instructions per chunk
     struct Chunk {
       u32x4_t kc[kLdsKeys ? kGroups + 1 : kGroups];
       uint32_t ks[kLdsKeys ? 1 : kGroups];
@@ -202,9 +217,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
       __amdgpu_buffer_rsrc_t r = rs;
       int co = lb * CSA2_IDX_BYTES;
       if constexpr (PAGED) {
-        const int c = (lb - wave * 64) / (kWaves * 64);   // the wave's chunk index (uniform)
+        // The chunk index, page and entry count are the same on every lane; readfirstlane
+        // says so, which keeps the descriptor in scalar registers (otherwise every load
+        // becomes a loop over the lanes' distinct descriptors).
+        const int c = __builtin_amdgcn_readfirstlane((lb - wave * 64) / (kWaves * 64));
         const int64_t page = __builtin_amdgcn_readlane(pv, c);
-        const int cnt = min(64, wg_n - lb);
+        const int cnt = __builtin_amdgcn_readfirstlane(max(0, min(64, wg_n - lb)));
         r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.idx_k + page * (CSA2_BLOCK * CSA2_IDX_BYTES)),
                                               (short)0, cnt * CSA2_IDX_BYTES, kRsrcWord3);
         co = 0;
@@ -226,120 +244,202 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MAXPAIRS ==
         }
       }
     };
-    __shared__ __align__(16) uint32_t kstage[kLdsKeys ? kWaves : 1][kLdsKeys ? 64 * CSA2_IDX_BYTES / 4 : 4];
+    // Contiguous reads: each wave's loaded chunk is stored to its LDS slot of 64 x 68
+    // bytes and read back in the MFMA lane layout.
+    constexpr int kStageWords = 64 * CSA2_IDX_BYTES / 4;
+    __shared__ __align__(16) uint32_t kstage[kLdsKeys ? kWaves : 1][kLdsKeys ? kStageWords : 4];
     bf16x8_t qa[MAXPAIRS][4];
     float wv[MAXPAIRS][4];
     const int nrows = r1 - r0;
     // Scores are staged in LDS: with at most kWgRows rows the whole workgroup's scores
     // stay until the end and leave as contiguous row segments (one write burst per
     // workgroup); with more rows each wave flushes every chunk.
+    // The contiguous path runs one row per request (a single stage row).
     constexpr bool kWgStage = CSA2_SCAN_WG_STAGE && 2 * MAXPAIRS <= kWgRows;
-    constexpr int kStageRows = kWgStage ? 2 * MAXPAIRS : 1;
+    constexpr int kStageRows = kWgStage ? (LDSK ? 1 : 2 * MAXPAIRS) : 1;
     constexpr int kStageLen = kWgStage ? kWaves * 64 * (LDSK && PARTS == 1 ? kMaxItersLdsk : kMaxIters) : 1;
     __shared__ __align__(16) float wstage[kStageRows][kStageLen];
     __shared__ __align__(16) float sbuf[kWgStage ? 1 : kWaves][2 * MAXPAIRS][64];
     float (*sb)[64] = sbuf[kWgStage ? 0 : wave];
-    auto consume = [&](const Chunk& ck, int lb) {
+    // Scores of one chunk (16 x kGroups entries) from its codes and scale bytes in the
+    // MFMA lane layout.
+    // Scores of one chunk (16 x kGroups entries) from its codes in the MFMA lane layout
+    // and each group's scale as the cvt operand (an fp32 whose exponent field is the
+    // E8M0 code).
+    __shared__ float wtrash[kWgStage && MAXPAIRS == 1 ? 64 : 1];
+    auto score_chunk = [&](const u32x4_t (&kcv)[kGroups], const float (&sc)[kGroups], int lb) {
+      if constexpr (MAXPAIRS == 1 && kWgStage) {
+        // One row pair: the groups' four-step MFMA chains run interleaved (no result is
+        // read right after the MFMA that writes it); the two half-sums meet through a
+        // row swap of the wave (first = rows 0 and 2, second = rows 1 and 3, so every
+        // lane ends with its pair's sum); every lane stores, the lanes that hold no
+        // staged score to a scratch word, so no store is branched around.
+        f32x4_t acc[kGroups];
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) acc[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int gi = 0; gi < kGroups; ++gi) acc[gi] = mfma16x16x32(qa[0][c], fp4x8_to_bf16(kcv[gi][c], sc[gi]), acc[gi]);
+        }
+        const int srow = LDSK ? 0 : (g >> 1);
+        const bool real = LDSK ? g == 0 : (g & 1) == 0;
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            part = fmaf(wv[0][i], __int_as_float(max(__float_as_int(acc[gi][i]), 0)), part);
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+          float* dst = real ? &wstage[srow][lb + 16 * gi + m] : &wtrash[lane];
+          *dst = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+          bf16x8_t kb[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kb[c] = fp4x8_to_bf16(kcv[gi][c], sc[gi]);
+#pragma unroll
+          for (int p = 0; p < MAXPAIRS; ++p) {
+            if (p < npairs) {
+              f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc = mfma16x16x32(qa[p][c], kb[c], acc);
+              const float sv = head_sum(acc, wv[p]);
+              if ((g & 1) == 0) {
+                if constexpr (kWgStage)
+                  wstage[2 * p + (g >> 1)][lb + 16 * gi + m] = sv;
+                else
+                  sb[2 * p + (g >> 1)][16 * gi + m] = sv;
+              }
+            }
+          }
+        }
+        if constexpr (!kWgStage) flush_chunk<MAXPAIRS>(sb, nrows, r0, wg_base + lb, n, a.scores, a.ld);
+      }
+    };
+    // A chunk in a slot, read in the MFMA lane layout: lane (m, g) of group gi takes
+    // entry 16gi + m's bytes 16g .. 16g+15 and its scale byte g, which one rotate (right
+    // by 8g + 9) moves to the fp32 exponent field.
+    const int srot = (8 * g + 9) & 31;
+    auto score_slot = [&](const uint32_t* kst, int lb) {
       u32x4_t kcv[kGroups];
-      uint32_t ksv[kGroups];
+      float sc[kGroups];
+#pragma unroll
+      for (int gi = 0; gi < kGroups; ++gi) {
+        const uint32_t* w = kst + (16 * gi + m) * (CSA2_IDX_BYTES / 4);
+        kcv[gi] = u32x4_t{w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]};
+        sc[gi] = __uint_as_float(__builtin_amdgcn_alignbit(w[16], w[16], srot) & 0x7F800000u);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      score_chunk(kcv, sc, lb);
+    };
+    // Register path of the contiguous reads: the loaded chunk goes to the wave's slot.
+    auto stage = [&](const Chunk& ck) {
       if constexpr (kLdsKeys) {
-        // Through the wave's LDS stage: lane (m, g) of group gi takes entry 16gi + m's
-        // bytes 16g .. 16g+15 and its scale byte g (the layout the direct loads give).
         uint32_t* kst = kstage[wave];
 #pragma unroll
         for (int q = 0; q < kGroups; ++q) *reinterpret_cast<u32x4_t*>(kst + 4 * lane + 256 * q) = ck.kc[q];
         if (lane < 16) *reinterpret_cast<u32x4_t*>(kst + 1024 + 4 * lane) = ck.kc[kGroups];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int gi = 0; gi < kGroups; ++gi) {
-          const uint32_t* w = kst + (16 * gi + m) * (CSA2_IDX_BYTES / 4);
-          kcv[gi] = u32x4_t{w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]};
-          ksv[gi] = (w[16] >> (8 * g)) & 0xFFu;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    };
+    auto consume = [&](const Chunk& ck, int lb) {
+      if constexpr (kLdsKeys) {
+        stage(ck);
+        score_slot(kstage[wave], lb);
       } else {
+        u32x4_t kcv[kGroups];
+        float sc[kGroups];
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi) {
           kcv[gi] = ck.kc[gi];
-          ksv[gi] = ck.ks[gi];
+          sc[gi] = e8m0_operand(ck.ks[gi]);
         }
+        score_chunk(kcv, sc, lb);
       }
-#pragma unroll
-      for (int gi = 0; gi < kGroups; ++gi) {
-        const float sc = e8m0_operand(ksv[gi]);
-        bf16x8_t kb[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kb[c] = fp4x8_to_bf16(kcv[gi][c], sc);
-#pragma unroll
-        for (int p = 0; p < MAXPAIRS; ++p) {
-          if (p < npairs) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc = mfma16x16x32(qa[p][c], kb[c], acc);
-            const float sv = head_sum(acc, wv[p]);
-            if ((g & 1) == 0) {
-              if constexpr (kWgStage)
-                wstage[2 * p + (g >> 1)][lb + 16 * gi + m] = sv;
-              else
-                sb[2 * p + (g >> 1)][16 * gi + m] = sv;
-            }
-          }
-        }
-      }
-      if constexpr (!kWgStage) flush_chunk<MAXPAIRS>(sb, nrows, r0, wg_base + lb, n, a.scores, a.ld);
     };
     constexpr int kStep = kWaves * 64;
     const int lb0 = wave * 64;
     if (lb0 < wg_n) {
+      // Start: the first chunks' loads, then the query (and wave 0's own block
+      // summaries), then one wait for all of them, so that inside the loop no register
+      // loaded before it makes the compiler wait for every load in flight.  ALL: every
+      // ring slot is filled (chunks past the workgroup's entries read zeros through the
+      // descriptor and are never scored).
       Chunk ring[kDepth];
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d)
-        if (d < iters && lb0 + d * kStep < wg_n) issue(ring[d], lb0 + d * kStep);
-      // Both parts in one launch without block tiles: the workgroup's own 64-entry
-      // blocks (4 x iters <= 16, one MFMA group) are scored by wave 0, their summaries
-      // loaded with its first chunk.
       bf16x8_t kbs[4];
-      int64_t jb0 = 0, jend = 0, bl0 = 0;
+      int64_t jb0 = 0, jend = 0;
+      // Both parts in one launch without block tiles: the workgroup's own 64-entry
+      // blocks (4 x iters <= 16, one MFMA group) are scored by wave 0.
       bool own_blocks = PARTS == 3 && a.block_tiles == 0 && wave == 0;   // uniform per wave
-      if constexpr (PARTS == 3) {
-        if (own_blocks) {
-          int64_t nb;
-          req_blocks(a.g, b, n, bl0, nb, PAGED);
-          jb0 = wg_base / CSA2_BLOCK;
-          jend = min<int64_t>(nb, (wg_base + wg_n + CSA2_BLOCK - 1) / CSA2_BLOCK);
-          // None of the workgroup's blocks in the pool: nothing to score (this also keeps
-          // the clamped row below in bounds).
-          own_blocks = jend > jb0;
-        }
-        if (own_blocks) {
-          const int64_t j = jb0 + m;
-          const int64_t jl = j < jend ? j : jend - 1;
-          const int64_t row = PAGED ? page_of(a.g, b, jl) : bl0 + jl;
-          const uint16_t* sp = a.blk_sum + row * CSA2_IDX_D + 32 * g;
+      auto start = [&](auto all) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) kbs[c] = as_bf16x8(load16(sp + 8 * c));
-        }
-      }
-      load_query<MAXPAIRS>(a, r0, r1, qa, wv);
-      if constexpr (PARTS == 3) {
-        if (own_blocks) score_group<MAXPAIRS>(kbs, qa, wv, npairs, r0, r1, jb0 + m, jend, a.blk_scores, a.blk_ld);
-      }
-      for (int c0 = 0; c0 < iters; c0 += kDepth) {
-        bool done = false;
+        for (int d = 0; d < kDepth; ++d)
+          if (decltype(all)::value || d < iters) issue(ring[d], lb0 + d * kStep);
+        if constexpr (PARTS == 3) {
+          int64_t bl0 = 0;
+          if (own_blocks) {
+            int64_t nb;
+            req_blocks(a.g, b, n, bl0, nb, PAGED);
+            jb0 = wg_base / CSA2_BLOCK;
+            jend = min<int64_t>(nb, (wg_base + wg_n + CSA2_BLOCK - 1) / CSA2_BLOCK);
+            // None of the workgroup's blocks in the pool: nothing to score (this also
+            // keeps the clamped row below in bounds).
+            own_blocks = jend > jb0;
+          }
+          if (own_blocks) {
+            const int64_t j = jb0 + m;
+            const int64_t jl = j < jend ? j : jend - 1;
+            const int64_t row = PAGED ? page_of(a.g, b, jl) : bl0 + jl;
+            const uint16_t* sp = a.blk_sum + row * CSA2_IDX_D + 32 * g;
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-          const int c = c0 + d, lb = lb0 + c * kStep;
-          if (!done && c < iters && lb < wg_n) {
-            consume(ring[d], lb);
-            const int ln = lb + kDepth * kStep;
-            if (c + kDepth < iters && ln < wg_n) issue(ring[d], ln);
-          } else {
-            done = true;
+            for (int c = 0; c < 4; ++c) kbs[c] = as_bf16x8(load16(sp + 8 * c));
           }
         }
-        if (done) break;
+        load_query<MAXPAIRS>(a, r0, r1, qa, wv);
+        wait_vmcnt<0>();
+        if constexpr (PARTS == 3) {
+          if (own_blocks) score_group<MAXPAIRS>(kbs, qa, wv, npairs, r0, r1, jb0 + m, jend, a.blk_scores, a.blk_ld);
+        }
+      };
+      if (iters <= kDepth) {
+        // Every chunk of the wave fits the ring: no refills.
+        start(std::false_type{});
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          const int lb = lb0 + d * kStep;
+          if (d < iters && lb < wg_n) consume(ring[d], lb);
+        }
+      } else if constexpr (kLdsKeys) {
+        // One chunk in registers: once it is staged to LDS the next chunk's loads go out
+        // before this chunk is scored (64 x 65,536-entry scan 53.1-55.2 -> 51.8-53.6 us
+        // over runs of 200 launches; scoring first and then loading was the slower order).
+        start(std::true_type{});
+        for (int c = 0; c < iters; ++c) {
+          const int lb = lb0 + c * kStep;
+          if (lb >= wg_n) break;
+          wait_vmcnt<0>();
+          stage(ring[0]);
+          issue(ring[0], lb + kStep);
+          score_slot(kstage[wave], lb);
+        }
+      } else {
+        // The ring's slots are consumed in turn (no data-dependent exit inside the
+        // unrolled ring) and every slot is refilled right after, so the waits before a
+        // chunk leave the kDepth - 1 chunks issued after it in flight.
+        start(std::true_type{});
+        for (int c0 = 0; c0 < iters; c0 += kDepth) {
+#pragma unroll
+          for (int d = 0; d < kDepth; ++d) {
+            const int lb = lb0 + (c0 + d) * kStep;
+            if (c0 + d < iters && lb < wg_n) consume(ring[d], lb);
+            issue(ring[d], lb + kDepth * kStep);
+          }
+        }
       }
     }
     if constexpr (kWgStage) {
@@ -438,7 +538,7 @@ static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid,
   // steps 117.7 -> 110.9 us at 64 x 128K, 105.7 -> 97.7 us at 1M context; short
   // workgroups were slower with them).
   if constexpr ((PARTS == 3 || PARTS == 1) && !PAGED) {
-    if (max_rows_per_req <= 2 && a.iters >= kMaxIters) {
+    if (max_rows_per_req == 1 && a.iters >= kMaxIters) {
       k_scan<1, PARTS, PAGED, true><<<grid, dim3(256), 0, st>>>(a);
       return;
     }
@@ -475,7 +575,7 @@ hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool bloc
   while (iters < kMaxIters && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
   // Entry-only scans that take the contiguous-read path (see launch_scan_rows) keep
   // doubling up to kMaxItersLdsk.
-  if (entries && !blocks && !a.g.page_table && max_rows_per_req <= 2 && iters >= kMaxIters)
+  if (entries && !blocks && !a.g.page_table && max_rows_per_req == 1 && iters >= kMaxIters)
     while (iters < kMaxItersLdsk && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
   a.iters = iters;
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;

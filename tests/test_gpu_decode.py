@@ -315,3 +315,44 @@ def test_decode_bits_do_not_depend_on_the_grid(csa2):
         if a.dtype == np.float32:
             a, b = a.view(np.uint32), b.view(np.uint32)
         assert np.array_equal(a, b), key
+
+
+def _judge_candidate_scores(wl, got, refs, rows):
+    # In the candidate-only scan only the kept blocks' entries the row sees are scored.
+    for r, ref in zip(rows, refs):
+        nk = int(got["n_kept"][r])
+        n = wl.n_entries(int(wl.row_req[r]))
+        pos = np.concatenate([np.arange(64 * j, min(64 * j + 64, n)) for j in got["kept"][r, :nk]])
+        want = ref["scores"][pos]
+        err = np.abs(got["scores"][r, pos] - want).max() / np.abs(want).mean()
+        assert err <= 1e-5, f"row {r}: candidate score error {err:.3g}"
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_candidate_only_scan_matches_oracle(csa2, cfg):
+    # scan_mode 1: the coarse stage runs first and only the kept blocks' keys are
+    # scored; the selected set is the full scan's by construction, and the whole row is
+    # judged against the oracle (128K context, and the 1M-context batch).
+    wl = make_config(cfg)
+    _log(f"candidate-only scan, config {cfg} ({wl.name}): {wl.num_rows} rows, {wl.total_entries} entries")
+    got = run_decode(csa2, wl, scan_mode=1)
+    rows = list(range(wl.num_rows))
+    refs = oracle.decode(wl)
+    judge(wl, got, refs)
+    _judge_candidate_scores(wl, got, refs, rows)
+
+
+def test_candidate_only_scan_on_sampled_64x128k_rows(csa2):
+    # The 64 x 128K batch bench.py times in candidate-only mode: sampled rows against the
+    # oracle, and every row's selection equal to the full scan's.
+    wl = make_config(5)
+    _log(f"candidate-only scan, 64 x 128K batch: {wl.total_entries} entries")
+    got = run_decode(csa2, wl, scan_mode=1)
+    full = run_decode(csa2, wl)
+    assert np.array_equal(got["kept"], full["kept"]) and np.array_equal(got["n_kept"], full["n_kept"])
+    assert np.array_equal(got["sel"], full["sel"]) and np.array_equal(got["n_sel"], full["n_sel"])
+    assert np.array_equal(got["out"].view(np.uint32), full["out"].view(np.uint32))
+    rows = [0, 17, 40, 63]
+    refs = oracle.decode(wl, rows=rows)
+    judge(wl, got, refs, rows=rows)
+    _judge_candidate_scores(wl, got, refs, rows)
