@@ -12,6 +12,7 @@
 // operand holds two query rows (8 heads each), so the rows of one request (verify
 // rows) share a single read of its keys.  The ReLU and the head weights are applied to
 // the fp32 MFMA output and the two half-sums meet with one cross-lane add.
+#include <algorithm>
 #include <type_traits>
 
 #include "csa2_internal.h"
@@ -37,9 +38,14 @@ typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
 #define CSA2_SCAN_WG_STAGE 1
 #endif
 constexpr int kMaxIters = CSA2_SCAN_MAX_ITERS;      // chunks per wave, at most
-// Entry-only scans on the contiguous-read path go to 8 chunks per wave (50.7-50.8 us on
-// the 64 x 65,536-entry scan against 51.6 at 4).
-constexpr int kMaxItersLdsk = 8;
+// Entry-only scans on the contiguous-read path: up to 14 chunks per wave, so that the
+// stage (14 KiB) and the key slots (17 KiB) leave room for kLdskWgsPerCu workgroups per
+// CU in 160 KiB of LDS.
+constexpr int kMaxItersLdsk = 14;
+constexpr int kLdskWgsPerCu = 5;
+#ifndef CSA2_SCAN_ONE_ROUND
+#define CSA2_SCAN_ONE_ROUND 1
+#endif
 constexpr int kWgRows = 4;                          // rows staged per workgroup
 #ifndef CSA2_SCAN_WAVES_PER_EU
 #define CSA2_SCAN_WAVES_PER_EU 4
@@ -257,8 +263,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     // The contiguous path runs one row per request (a single stage row).
     constexpr bool kWgStage = CSA2_SCAN_WG_STAGE && 2 * MAXPAIRS <= kWgRows;
     constexpr int kStageRows = kWgStage ? (LDSK ? 1 : 2 * MAXPAIRS) : 1;
-    constexpr int kStageLen = kWgStage ? kWaves * 64 * (LDSK && PARTS == 1 ? kMaxItersLdsk : kMaxIters) : 1;
-    __shared__ __align__(16) float wstage[kStageRows][kStageLen];
+    // Entry-only contiguous-read scans size their stage at launch (dynamic LDS of
+    // iters x 1 KiB): their chunks per wave are chosen so that the grid is one round.
+    constexpr bool kDynStage = LDSK && PARTS == 1;
+    constexpr int kStageLen = kWgStage && !kDynStage ? kWaves * 64 * kMaxIters : 1;
+    __shared__ __align__(16) float wstage_s[kStageRows][kStageLen];
+    extern __shared__ __align__(16) float scan_dyn_stage[];
+    float* const wst = kDynStage ? scan_dyn_stage : &wstage_s[0][0];
+    const int wst_ld = kDynStage ? kWaves * 64 * iters : kStageLen;
     __shared__ __align__(16) float sbuf[kWgStage ? 1 : kWaves][2 * MAXPAIRS][64];
     float (*sb)[64] = sbuf[kWgStage ? 0 : wave];
     // Scores of one chunk (16 x kGroups entries) from its codes and scale bytes in the
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
           for (int i = 0; i < 4; ++i)
             part = fmaf(wv[0][i], __int_as_float(max(__float_as_int(acc[gi][i]), 0)), part);
           const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-          float* dst = real ? &wstage[srow][lb + 16 * gi + m] : &wtrash[lane];
+          float* dst = real ? &wst[srow * wst_ld + lb + 16 * gi + m] : &wtrash[lane];
           *dst = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
       } else {
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
               const float sv = head_sum(acc, wv[p]);
               if ((g & 1) == 0) {
                 if constexpr (kWgStage)
-                  wstage[2 * p + (g >> 1)][lb + 16 * gi + m] = sv;
+                  wst[(2 * p + (g >> 1)) * wst_ld + lb + 16 * gi + m] = sv;
                 else
                   sb[2 * p + (g >> 1)][16 * gi + m] = sv;
               }
@@ -447,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       for (int t = 0; t < nrows; ++t) {
         float* orow = a.scores + (int64_t)(r0 + t) * a.ld + wg_base;
         for (int i = 4 * (int)threadIdx.x; i < wg_n; i += 4 * kWaves * 64) {
-          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&wstage[t][i]);
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&wst[t * wst_ld + i]);
           if (i + 4 <= wg_n) {
             // A scan that only produces scores (PARTS 1) hands them to the caller: stream
             // them past the caches.  In the decode chain the select reads them next.
@@ -531,6 +543,18 @@ __global__ __launch_bounds__(64) void k_scan_kept(ScanArgs a) {
 
 }  // namespace
 
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
 template <int PARTS, bool PAGED>
 static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid, hipStream_t st) {
   // Contiguous key reads (LDSK) where they measured faster: long workgroups, one row
@@ -539,7 +563,8 @@ static void launch_scan_rows(const ScanArgs& a, int max_rows_per_req, dim3 grid,
   // workgroups were slower with them).
   if constexpr ((PARTS == 3 || PARTS == 1) && !PAGED) {
     if (max_rows_per_req == 1 && a.iters >= kMaxIters) {
-      k_scan<1, PARTS, PAGED, true><<<grid, dim3(256), 0, st>>>(a);
+      const size_t dyn = PARTS == 1 ? (size_t)kWaves * 64 * a.iters * sizeof(float) : 0;
+      k_scan<1, PARTS, PAGED, true><<<grid, dim3(256), dyn, st>>>(a);
       return;
     }
   }
@@ -573,10 +598,19 @@ hipError_t launch_scan(ScanArgs a, int max_rows_per_req, bool entries, bool bloc
   const int64_t tiles1 = (a.g.max_entries + kTile - 1) / kTile;
   int iters = 1;
   while (iters < kMaxIters && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
-  // Entry-only scans that take the contiguous-read path (see launch_scan_rows) keep
-  // doubling up to kMaxItersLdsk.
-  if (entries && !blocks && !a.g.page_table && max_rows_per_req == 1 && iters >= kMaxIters)
-    while (iters < kMaxItersLdsk && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
+  // Entry-only scans that take the contiguous-read path (see launch_scan_rows) run as
+  // one round of workgroups: kLdskWgsPerCu per CU, each wave taking as many chunks as
+  // that needs (a second, partly occupied round of workgroups would end the launch).
+  if (entries && !blocks && !a.g.page_table && max_rows_per_req == 1 && iters >= kMaxIters) {
+#if CSA2_SCAN_ONE_ROUND
+    const int64_t chunks = (a.g.max_entries + CSA2_BLOCK - 1) / CSA2_BLOCK;
+    const int64_t per_req = std::max<int64_t>(1, (int64_t)kLdskWgsPerCu * device_cus() / a.g.B);
+    const int64_t it = (chunks + kWaves * per_req - 1) / (kWaves * per_req);
+    iters = (int)std::min<int64_t>(std::max<int64_t>(it, kMaxIters), kMaxItersLdsk);
+#else
+    while (iters < 8 && tiles1 * a.g.B >= (int64_t)CSA2_SCAN_TARGET_WGS * 2 * iters) iters *= 2;
+#endif
+  }
   a.iters = iters;
   a.entry_tiles = entries ? (int32_t)((a.g.max_entries + (int64_t)kTile * iters - 1) / ((int64_t)kTile * iters)) : 0;
   a.blk_groups = iters < kGroups ? iters : kGroups;

@@ -264,19 +264,20 @@ def test_decode_with_workspace_at_the_end_of_an_allocation(csa2):
     judge(wl, got, oracle.decode(wl, n_keep=1), n_keep=1)
 
 
-def test_entry_scan_eight_chunks_per_wave_ragged(csa2):
-    # The entry-only scan over contiguous pools runs 8 chunks per wave (2,048-entry
-    # workgroups) once ceil(max_entries / 256) x B >= 16,384.  Lengths that are not
-    # multiples of 2,048 or 64 leave partial workgroups and chunks at every request's end.
-    # Scores equal the direct-load scan's (the same workload over paged pools) bit for
-    # bit, and sampled requests are judged against the oracle.
+def test_entry_scan_long_workgroups_ragged(csa2):
+    # The entry-only scan over contiguous pools sizes its workgroups so that the grid is
+    # one round of five per CU: here 13 chunks (832 entries) per wave, 3,328-entry
+    # workgroups (a multiple of neither 2,048 nor a power of two).  Lengths that are not
+    # multiples of 64 leave partial workgroups and chunks at every request's end.  Scores
+    # equal the direct-load scan's (the same workload over paged pools) bit for bit, and
+    # sampled requests are judged against the oracle.
     lens = [524288 + 37, 524288 - 1, 400003, 262144 + 64 * 5 + 1, 140001, 4097, 65, 524288 - 200]
-    tiles1, iters = -(-max(lens) // 256), 1
-    while iters < 8 and tiles1 * len(lens) >= 2048 * 2 * iters:
-        iters *= 2
-    assert iters == 8
+    chunks = -(-max(lens) // 64)
+    per_req = 5 * 256 // len(lens)
+    iters = min(max(-(-chunks // (4 * per_req)), 4), 14)
+    assert iters == 13
     wl = make_workload("ldsk8", 53, lens, rows_per_req=1, n_needles=8, scan_only=True)
-    _log(f"entry-only scan at 8 chunks per wave, ragged lengths {lens}")
+    _log(f"entry-only scan at {iters} chunks per wave, ragged lengths {lens}")
     dw = upload(wl)
     flat = csa2.index_score(dw.rg, dw.idx_k, dw.q_idx, dw.w).cpu().numpy()
     del dw
