@@ -306,6 +306,18 @@ int csa2_debug_mxfp8(const float* x, int64_t n, float* out, void* stream);
  * CSA2_ERR_INVALID_ARG for misaligned pointers or sizes. */
 int csa2_debug_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement hook, for callers that want the shader clock while other work runs (the
+ * clock falls under sustained load): one wave records n pairs (shader-clock counter,
+ * 100 MHz reference counter) into out[2i], out[2i+1], one pair every `interval`
+ * reference ticks (10 ns), and ends after n x interval ticks.  Launched on a stream of
+ * its own beside the work to observe; clock in GHz = 0.1 x (change of the first) /
+ * (change of the second).  out: device memory of 2n uint64, owned by the caller.
+ * Errors: CSA2_ERR_INVALID_ARG for n outside [0, CSA2_CLOCK_TRACE_MAX_SAMPLES], interval
+ * < 1, n x interval above CSA2_CLOCK_TRACE_MAX_TICKS (2 s), or a misaligned out. */
+#define CSA2_CLOCK_TRACE_MAX_SAMPLES 65536
+#define CSA2_CLOCK_TRACE_MAX_TICKS 200000000
+int csa2_debug_clock_trace(uint64_t* out, int32_t n, int32_t interval, void* stream);
+
 const char* csa2_status_string(int32_t status);
 const char* csa2_last_error(void);
 int32_t csa2_version(void);

@@ -65,7 +65,8 @@ class _DecodeArgs(ctypes.Structure):
 
 EXPORTS = ("csa2_index_score", "csa2_block_filter", "csa2_topk", "csa2_sparse_attn", "csa2_cache_write",
            "csa2_sparse_attn_workspace_size", "csa2_decode", "csa2_decode_workspace_size", "csa2_decode_static",
-           "csa2_debug_dequant", "csa2_debug_mxfp8", "csa2_debug_stream_read", "csa2_status_string", "csa2_last_error",
+           "csa2_debug_dequant", "csa2_debug_mxfp8", "csa2_debug_stream_read", "csa2_debug_clock_trace",
+           "csa2_status_string", "csa2_last_error",
            "csa2_version")
 
 _lib = None
@@ -93,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "csa2_decode_static": ([DA, P], ctypes.c_int),
         "csa2_debug_dequant": ([I32, P, P, I64, P, P], ctypes.c_int),
         "csa2_debug_stream_read": ([P, I64, P, P], ctypes.c_int),
+        "csa2_debug_clock_trace": ([P, I32, I32, P], ctypes.c_int),
         "csa2_debug_mxfp8": ([P, I64, P, P], ctypes.c_int),
         "csa2_cache_write": ([RG, P, P, P, P, P, P, P, F32, P, P, P, P], ctypes.c_int),
         "csa2_status_string": ([I32], ctypes.c_char_p),
@@ -370,6 +372,16 @@ def debug_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
     _dev(sink, (torch.int32,), "sink")
     nbytes = src.numel() * src.element_size()
     _check(lib.csa2_debug_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream()))
+
+
+def debug_clock_trace(out: torch.Tensor, n: int, interval: int) -> None:
+    """Shader-clock samples on the current stream: out[2i] = shader-clock counter,
+    out[2i+1] = 100 MHz reference counter, one pair every ``interval`` reference ticks."""
+    lib = load_library()
+    _dev(out, (torch.int64,), "out")
+    if out.numel() < 2 * n:
+        raise ValueError("out holds fewer than 2n values")
+    _check(lib.csa2_debug_clock_trace(_ptr(out), int(n), int(interval), _stream()))
 
 
 def cache_write(rg: Ragged, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, main_kv, idx_k,

@@ -212,6 +212,29 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hi
   return hipGetLastError();
 }
 
+// Clock sampler: one wave reads the shader-clock counter and the 100 MHz reference
+// counter every `interval` reference ticks, n times, and lane 0 stores each pair.  The
+// wait between samples is bounded by the reference counter, so the kernel ends after
+// n x interval ticks.
+__global__ __launch_bounds__(64) void k_clock_trace(uint64_t* out, int n, int interval) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < n; ++i) {
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    const uint64_t r = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+      out[2 * i] = t;
+      out[2 * i + 1] = r;
+    }
+    const uint64_t until = r0 + (uint64_t)(i + 1) * (uint64_t)interval;
+    while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+hipError_t launch_clock_trace(uint64_t* out, int n, int interval, hipStream_t st) {
+  k_clock_trace<<<dim3(1), dim3(64), 0, st>>>(out, n, interval);
+  return hipGetLastError();
+}
+
 // Test hook: lane (i, g) of a wave rounds values 8g .. 8g+7 of block 16w + i (w = the
 // wave's index in the grid) with the attention kernel's block helper.
 __global__ __launch_bounds__(256) void k_debug_mxfp8(const float* x, int64_t nblocks, float* out) {
@@ -655,6 +678,16 @@ int csa2_debug_stream_read(const void* src, int64_t bytes, uint32_t* sink, void*
   CHECK(check_ptr(src, 16, "src"));
   CHECK(check_ptr(sink, 4, "sink"));
   LAUNCH(launch_stream_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream)), "stream read");
+  return CSA2_OK;
+}
+
+int csa2_debug_clock_trace(uint64_t* out, int32_t n, int32_t interval, void* stream) {
+  if (n < 0 || n > CSA2_CLOCK_TRACE_MAX_SAMPLES) return fail(CSA2_ERR_INVALID_ARG, "n out of range");
+  if (interval < 1 || (int64_t)n * interval > CSA2_CLOCK_TRACE_MAX_TICKS)
+    return fail(CSA2_ERR_INVALID_ARG, "interval out of range");
+  if (n == 0) return CSA2_OK;
+  CHECK(check_ptr(out, 8, "out"));
+  LAUNCH(launch_clock_trace(out, n, interval, reinterpret_cast<hipStream_t>(stream)), "clock trace");
   return CSA2_OK;
 }
 

@@ -210,6 +210,7 @@ hipError_t launch_cache_write(const RaggedDev& g, const int64_t* row_pos, const 
                               const float* gamma_idx, float eps, uint8_t* main_kv, uint8_t* idx_k, uint16_t* blk_sum,
                               hipStream_t st);
 hipError_t launch_debug_mxfp8(const float* x, int64_t n, float* out, hipStream_t st);
+hipError_t launch_clock_trace(uint64_t* out, int n, int interval, hipStream_t st);
 hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,
                                 hipStream_t st);
 

@@ -138,6 +138,16 @@ def test_stream_read_validates_before_launch(lib):
     assert lib.csa2_debug_stream_read(0x10008, 16, 0x20000, None) == csa2.ERR_INVALID_ARG  # misaligned
 
 
+def test_clock_trace_validates_before_launch(lib):
+    assert lib.csa2_debug_clock_trace(None, 0, 1, None) == csa2.OK
+    assert lib.csa2_debug_clock_trace(None, -1, 1, None) == csa2.ERR_INVALID_ARG
+    assert lib.csa2_debug_clock_trace(0x10000, 4, 0, None) == csa2.ERR_INVALID_ARG       # interval < 1
+    assert lib.csa2_debug_clock_trace(0x10000, 65537, 1, None) == csa2.ERR_INVALID_ARG   # too many samples
+    assert lib.csa2_debug_clock_trace(0x10000, 4000, 100000, None) == csa2.ERR_INVALID_ARG  # 4 s
+    assert lib.csa2_debug_clock_trace(None, 4, 10, None) == csa2.ERR_INVALID_ARG         # null out
+    assert lib.csa2_debug_clock_trace(0x10004, 4, 10, None) == csa2.ERR_INVALID_ARG      # misaligned
+
+
 def test_paged_descriptor_checks(lib):
     fake = 0x10000
     args = (16, 16, 16, None, None, 0, 16, 100, None)

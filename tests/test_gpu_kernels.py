@@ -286,3 +286,20 @@ def test_sparse_attn_skips_invalid_positions(csa2):
                                     wl.sm_scale)
     rel, dl = parity.attn_error(out.cpu().numpy()[0], lse.cpu().numpy()[0], ro, rl)
     assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS
+
+
+def test_clock_trace_samples(csa2):
+    _log("clock trace: 64 samples 2 us apart")
+    n, interval = 64, 200
+    out = torch.zeros(2 * n + 2, dtype=torch.int64, device="cuda")
+    csa2.debug_clock_trace(out, n, interval)
+    torch.cuda.synchronize()
+    v = out.cpu().numpy()
+    t, r = v[0:2 * n:2].astype(np.float64), v[1:2 * n:2].astype(np.float64)
+    assert v[2 * n] == 0 and v[2 * n + 1] == 0, "wrote past 2n values"
+    # Sample i waits until i x interval ticks after the start, so samples are at least that
+    # far apart in total (one may land late and the next on time).
+    assert np.all(np.diff(t) > 0) and np.all(np.diff(r) > 0) and r[-1] - r[0] >= (n - 2) * interval
+    ghz = 0.1 * (t[-1] - t[0]) / (r[-1] - r[0])
+    _log(f"  shader clock {ghz:.2f} GHz over {(r[-1] - r[0]) / 100:.0f} us")
+    assert 0.3 < ghz < 3.0
