@@ -28,7 +28,11 @@
 namespace csa2 {
 namespace {
 
-constexpr int KLS = 528;        // Kl row stride in bf16 (512 + 16: rows 32 B apart modulo 256 B)
+#ifndef CSA2_ATTN_KLS
+#define CSA2_ATTN_KLS 528
+#endif
+constexpr int KLS = CSA2_ATTN_KLS;   // Kl row stride in bf16 (512 + 16: rows 32 B apart modulo 256 B)
+static_assert(KLS >= 512 && KLS % 8 == 0, "Kl rows hold 512 bf16, 16-byte aligned");
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplitKeys = CSA2_K_MAX + CSA2_SWA_MAX;   // positions of one split staged in LDS
 constexpr int kAttnTileKeys = 64;
@@ -294,8 +298,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
         mx = fmaxf(mx, z[4 * b + i]);
       }
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = xor32_max(xor16_max(mx));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
@@ -356,8 +359,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     __syncthreads();   // LDS reads of this tile are done before the next tile's writes
   }
 
-  float l_tot = l_run + shfl_xor_f(l_run, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  const float l_tot = xor32_add(xor16_add(l_run));
   // Lane holds O^T[256dh + 16t + 4g + i][h].
   if (a.splits == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

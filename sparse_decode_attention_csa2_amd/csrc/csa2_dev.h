@@ -53,20 +53,50 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 -> two bf16 (round half to even; a in the low half): one v_cvt_pk_bf16_f32.
+// Equal to bf16_bits_rne on both for finite inputs (fp32 denormals are preserved).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{a, b}), b2_t));
+}
+
 // Split 8 fp32 values into bf16 hi + lo parts (v ~= hi + lo to about 2^-17 relative),
-// packed as MFMA operands.  Integer packing only.
+// packed as MFMA operands: hi = RNE(v), lo = RNE(v - hi).
 __device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
   u32x4_t hw, lw;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t h0 = bf16_bits_rne(v[2 * q]), h1 = bf16_bits_rne(v[2 * q + 1]);
-    const float r0 = v[2 * q] - __uint_as_float(h0 << 16);
-    const float r1 = v[2 * q + 1] - __uint_as_float(h1 << 16);
-    hw[q] = h0 | (h1 << 16);
-    lw[q] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
+    const uint32_t h = pack_bf16x2_rne(v[2 * q], v[2 * q + 1]);
+    const float r0 = v[2 * q] - __uint_as_float(h << 16);
+    const float r1 = v[2 * q + 1] - __uint_as_float(h & 0xFFFF0000u);
+    hw[q] = h;
+    lw[q] = pack_bf16x2_rne(r0, r1);
   }
   hi = __builtin_bit_cast(bf16x8_t, hw);
   lo = __builtin_bit_cast(bf16x8_t, lw);
+}
+
+// Max / sum of x over lanes l and l ^ 16, and over lanes l and l ^ 32, through gfx950's
+// row and half swaps (VALU, no LDS round trip).  v_permlane16_swap of x with itself
+// gives every lane the values of its 16-lane row pair (even row first), and
+// v_permlane32_swap those of its two 32-lane halves (lower half first); max and sum are
+// symmetric, so every lane gets the same bits as x op shuffle(x).
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_add(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 // ---------------------------------------------------------------------------------
@@ -102,8 +132,7 @@ __device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) 
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  amax = xor32_max(xor16_max(amax));
   const int s = mx8_scale_exp(amax);
   u32x4_t w;
 #if CSA2_MX_HW_CVT
@@ -113,10 +142,10 @@ __device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) 
   const float sc = __builtin_ldexpf(1.f, s), lim = __builtin_ldexpf(448.f, s);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float a = fminf(fmaxf(v[2 * q], -lim), lim), b = fminf(fmaxf(v[2 * q + 1], -lim), lim);
+    const float a = __builtin_amdgcn_fmed3f(v[2 * q], -lim, lim), b = __builtin_amdgcn_fmed3f(v[2 * q + 1], -lim, lim);
     const v2s p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, sc, false);
     const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)__builtin_bit_cast(int, p), sc, false);
-    w[q] = bf16_bits_rne(f[0]) | (bf16_bits_rne(f[1]) << 16);
+    w[q] = pack_bf16x2_rne(f[0], f[1]);
   }
 #else
 #pragma unroll
@@ -172,6 +201,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
 
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no LDS round
 // trips): row_shr 1/2/4/8 scans each row of 16 lanes, then row_bcast15 and row_bcast31
