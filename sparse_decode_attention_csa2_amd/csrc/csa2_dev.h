@@ -125,15 +125,9 @@ __device__ __forceinline__ float mx8_round(float x, int s) {
   return copysignf(__builtin_ldexpf(fminf(r, 448.f), s), x);
 }
 
-// MXFP8-round 8 fp32 values of a 32-value block whose other 24 values sit in the lanes
-// xor 16 and xor 32 (a lane's 8 values are one quarter of the block), packed as an exact
-// bf16 MFMA operand (element q in the low half of word q / 2).
-__device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) {
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  amax = xor32_max(xor16_max(amax));
-  const int s = mx8_scale_exp(amax);
+// MXFP8-round 8 fp32 values of a block with shared exponent s, packed as an exact bf16
+// MFMA operand (element q in the low half of word q / 2).
+__device__ __forceinline__ bf16x8_t mx8_round8_bf16x8(const float (&v)[8], int s) {
   u32x4_t w;
 #if CSA2_MX_HW_CVT
   // gfx950's scaled FP8 conversions: x / 2^s to E4M3FN (round to nearest even) and back
@@ -153,6 +147,16 @@ __device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) 
     w[q] = bf16_bits_rne(mx8_round(v[2 * q], s)) | (bf16_bits_rne(mx8_round(v[2 * q + 1], s)) << 16);
 #endif
   return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// MXFP8-round 8 fp32 values of a 32-value block whose other 24 values sit in the lanes
+// xor 16 and xor 32 (a lane's 8 values are one quarter of the block).
+__device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = xor32_max(xor16_max(amax));
+  return mx8_round8_bf16x8(v, mx8_scale_exp(amax));
 }
 
 // Widen 8 bf16 to fp32 through the packed 32-bit words (integer shifts only).

@@ -84,12 +84,12 @@ __device__ __forceinline__ void load_query(const ScanArgs& a, int r0, int r1, bf
 
 // Weighted ReLU over the lane's 4 heads, then the partner half (lane ^ 16).  The ReLU
 // is an integer max on the fp32 bits (negative floats are negative integers), and the
-// exchange is a swizzle (xor 16 within each 32-lane half).
+// exchange is a row swap (VALU; every lane gets the same sum).
 __device__ __forceinline__ float head_sum(const f32x4_t& acc, const float (&wv)[4]) {
   float part = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) part = fmaf(wv[i], __int_as_float(max(__float_as_int(acc[i]), 0)), part);
-  return part + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(part), 0x401F));
+  return xor16_add(part);
 }
 
 template <int MAXPAIRS>
