@@ -138,7 +138,9 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 // reads its A operand (V^T) from the same key-major copy with transposing LDS loads.
 // MX: the MXFP8 route (Q and P rounded to MXFP8 before their products); otherwise Q as
 // given and P as exact-to-2^-17 bf16 hi + lo parts.
-template <bool MX, bool ROWS>
+// HALF: the plan ends some splits with a half-full tile (split_keys not a multiple of
+// the tile), so tiles check for it; other plans get no trace of that path.
+template <bool MX, bool ROWS, bool HALF>
 __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   constexpr int TK = kAttnTileKeys;   // 64
   constexpr int KB = TK / 32;         // 32-key groups
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), hg = wave & 3, dh = wave >> 2;
   const int h = hg * 16 + ln;
-  const int k_begin = split * a.tiles_per_split * TK;
+  const int k_begin = split * a.split_keys;
 
   // Dequant role: keys 32u + 2kp + e (e < 2) of a tile, dims 32ch .. 32ch+31.  A tile's
   // keys are fetched in two steps that every thread takes without branching (so no load
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     return;
   }
   if (k_begin >= n_keys) return;
-  const int k_end = min(n_keys, k_begin + a.tiles_per_split * TK);
+  const int k_end = min(n_keys, k_begin + a.split_keys);
 
   f32x4_t o[16];
 #pragma unroll
@@ -259,17 +261,33 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     const bool more = kt + TK < k_end;
     if (more) sel_pos(kt + TK);
 
-    // Partial S^T over this wave's 256 dims: 16-key blocks b, 8 K steps of 32 dims.
+    // Partial S^T over this wave's 256 dims: 16-key blocks b, 8 K steps of 32 dims.  A
+    // tile holding at most 32 keys (the end of a split) skips its empty second half here
+    // and in PV: those keys are empty (zero records, masked logits), so the skipped
+    // products are exact zeros.
+    const bool half = HALF && kt + TK / 2 >= k_end;   // uniform
     f32x4_t s[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (half) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+      for (int st = 0; st < 8; ++st) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bf16x8_t ak =
-            as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + 8 * g));
-        s[b] = mfma16x16x32(ak, qb[st], s[b]);
+        for (int b = 0; b < NB / 2; ++b) {
+          const bf16x8_t ak =
+              as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+          s[b] = mfma16x16x32(ak, qb[st], s[b]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8_t ak =
+              as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+          s[b] = mfma16x16x32(ak, qb[st], s[b]);
+        }
       }
     }
     // The two dim halves of a head group meet in LDS.
@@ -338,6 +356,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     // 32c + 16 + 4g + {0..3} (the order of pb), read transposed from the key-major tile.
 #pragma unroll
     for (int c = 0; c < KB; ++c) {
+      if (half && c > 0) break;   // uniform: the second 32-key group is empty
 #pragma unroll
       for (int t0 = 0; t0 < 16; t0 += 4) {
         bf16x8_t av[4];
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const RowKeys rk = row_keys(a, r);
   const int n_keys = rk.n_main + rk.n_swa;
   if (n_keys == 0) return;
-  const int per = a.tiles_per_split * a.tile_keys;
+  const int per = a.split_keys;
   const int ns = (n_keys + per - 1) / per;
   const int tid = threadIdx.x, lane = tid & 63, tt = tid >> 6, ln = lane & 15, g = lane >> 4;
   const int h = 16 * w + ln, t = 4 * tg + tt;
@@ -451,8 +470,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 }  // namespace
 
 // Splits per row: enough workgroups to cover the GPU; a split takes its 64-key tiles
-// one after another.
-void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& tiles_per_split, int32_t& splits) {
+// one after another.  The number of splits comes from whole tiles; the keys are then
+// spread over them in 32-key units (at least one tile each), which shortens the longest
+// split where whole tiles divide unevenly (640 keys in 4 splits: 160 each, the last tile
+// of a split half-full, instead of 3 + 3 + 3 + 1 tiles; 64-row attention 33.2 -> 32.3 us).
+// A tile holding at most 32 keys runs only its first half.  Finer plans with more splits
+// measured slower (32 rows: 7 splits of 96 keys against 5 of 128, +2 us per step).
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits) {
   const int max_keys = sel_ld + CSA2_SWA_MAX;
   const int tk = kAttnTileKeys;
   const int tiles = (max_keys + tk - 1) / tk;
@@ -460,32 +484,45 @@ void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& tiles_per
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
   tile_keys = tk;
-  tiles_per_split = (int32_t)((tiles + want - 1) / want);
-  splits = (tiles + tiles_per_split - 1) / tiles_per_split;
+  const int64_t tps = (tiles + want - 1) / want;
+  const int64_t n = (tiles + tps - 1) / tps;
+  int64_t per = (max_keys + n - 1) / n;
+  per = (per + tk / 2 - 1) / (tk / 2) * (tk / 2);
+  if (per < tk) per = tk;
+  split_keys = (int32_t)per;
+  splits = (int32_t)((max_keys + per - 1) / per);
 }
 
 size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
-  int32_t tk, tps, splits;
-  attn_plan(R, sel_ld, tk, tps, splits);
+  int32_t tk, per, splits;
+  attn_plan(R, sel_ld, tk, per, splits);
   if (splits <= 1) return 0;
   const size_t parts = (size_t)R * splits * CSA2_HEADS;
   return parts * CSA2_D * sizeof(float) + 2 * parts * sizeof(float) + 3 * 256;
 }
 
+template <bool HALF>
+static void launch_attn_variant(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  if (a.qp_route == CSA2_QP_MXFP8) {
+    if (a.sel_rows)
+      k_attn<true, true, HALF><<<grid, dim3(512), 0, st>>>(a);
+    else
+      k_attn<true, false, HALF><<<grid, dim3(512), 0, st>>>(a);
+  } else {
+    if (a.sel_rows)
+      k_attn<false, true, HALF><<<grid, dim3(512), 0, st>>>(a);
+    else
+      k_attn<false, false, HALF><<<grid, dim3(512), 0, st>>>(a);
+  }
+}
+
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
   const dim3 grid(a.splits, a.g.R);
-  if (a.qp_route == CSA2_QP_MXFP8) {
-    if (a.sel_rows)
-      k_attn<true, true><<<grid, dim3(512), 0, st>>>(a);
-    else
-      k_attn<true, false><<<grid, dim3(512), 0, st>>>(a);
-  } else {
-    if (a.sel_rows)
-      k_attn<false, true><<<grid, dim3(512), 0, st>>>(a);
-    else
-      k_attn<false, false><<<grid, dim3(512), 0, st>>>(a);
-  }
+  if (a.split_keys % kAttnTileKeys != 0)
+    launch_attn_variant<true>(a, grid, st);
+  else
+    launch_attn_variant<false>(a, grid, st);
   return hipGetLastError();
 }
 

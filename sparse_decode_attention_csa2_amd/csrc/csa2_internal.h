@@ -186,7 +186,7 @@ struct AttnArgs {
   const float* swa_scale;
   float sm_scale_log2;       // sm_scale * log2(e)
   int32_t tile_keys;         // keys per tile (64)
-  int32_t tiles_per_split;
+  int32_t split_keys;        // keys per split: a multiple of 32, at least one tile
   int32_t splits;
   float* opart;              // [R][splits][8 waves][16 d-tiles][64 lanes][4]
   float* mpart;              // [R][splits][64]
@@ -195,7 +195,7 @@ struct AttnArgs {
   float* lse;                // [R][64]
 };
 
-void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& tiles_per_split, int32_t& splits);
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits);
 size_t attn_workspace_bytes(int64_t R, int32_t sel_ld);
 hipError_t launch_attn(AttnArgs a, hipStream_t st);
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st);

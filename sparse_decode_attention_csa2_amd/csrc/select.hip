@@ -29,9 +29,16 @@ namespace {
 
 constexpr int NT = 512;
 constexpr int NW = NT / kWave;
-constexpr int kBins = 2048;
-constexpr int kDigit = 11;
-constexpr int kMemMax = 256;                                 // bin members resolved directly
+#ifndef CSA2_SEL_DIGIT
+#define CSA2_SEL_DIGIT 11
+#endif
+#ifndef CSA2_SEL_MEMMAX
+#define CSA2_SEL_MEMMAX 256
+#endif
+constexpr int kDigit = CSA2_SEL_DIGIT;                       // key bits ranked per histogram pass
+constexpr int kBins = 1 << kDigit;
+static_assert(kBins >= 4 * kWave && kBins <= kWave * kWave, "bins per lane: 4 .. 64");
+constexpr int kMemMax = CSA2_SEL_MEMMAX;                     // bin members resolved directly
 constexpr int kMaxCand = (CSA2_KEEP_MAX + 1) * CSA2_BLOCK;   // 8256 candidate slots
 constexpr int kLdsBlocks = 16384;                            // block keys held in LDS
 constexpr int kGB = 16;                                      // gather batch per thread
@@ -113,25 +120,27 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     if (threadIdx.x == 0) sh.mcnt = 0;
     __syncthreads();
     if (wave == 0) {
-      // Lane l owns bins 2047-32l down to 2016-32l; find the bin holding the rem-th key.
-      const uint32_t* hb = hist + kBins - kBins / kWave * (lane + 1);
+      // Lane l owns the kPer bins below kBins - kPer * l (highest first); find the bin
+      // holding the rem-th key.
+      constexpr int kPer = kBins / kWave;
+      const uint32_t* hb = hist + kBins - kPer * (lane + 1);
       uint32_t tot = 0u;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kPer / 4; ++q) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hb + 4 * q);
         tot += v[0] + v[1] + v[2] + v[3];
       }
       const uint32_t before = wave_incl_scan(tot) - tot;
-      // The lane whose 32 bins hold the rem-th key; its bins are then examined by
-      // lanes 0..31 in parallel (lane x takes the x-th bin in descending order).
+      // The lane whose kPer bins hold the rem-th key; its bins are then examined by
+      // lanes 0 .. kPer-1 in parallel (lane x takes the x-th bin in descending order).
       const uint64_t owner = __ballot(before < (uint32_t)rem && before + tot >= (uint32_t)rem);
       const int tl = owner ? (int)__builtin_ctzll(owner) : kWave - 1;
       const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
-      const int x = lane & 31;
-      const uint32_t bin = (uint32_t)(kBins - kBins / kWave * (tl + 1) + (31 - x));
-      const uint32_t cnt = lane < 32 ? hist[bin] : 0u;
+      const int x = lane & (kPer - 1);
+      const uint32_t bin = (uint32_t)(kBins - kPer * (tl + 1) + (kPer - 1 - x));
+      const uint32_t cnt = lane < kPer ? hist[bin] : 0u;
       const uint32_t incl = tb + wave_incl_scan(cnt);
-      const uint64_t hit = __ballot(lane < 32 && incl >= (uint32_t)rem);
+      const uint64_t hit = __ballot(lane < kPer && incl >= (uint32_t)rem);
       if (lane == (int)__builtin_ctzll(hit)) {
         sh.digit = bin;
         sh.above = incl - cnt;
