@@ -12,8 +12,8 @@
 // 64; each wave owns a contiguous range of chunks, so item order is (wave, chunk, lane).
 //  - k-th largest key: keys are normalised by the workgroup minimum and an 11-bit
 //    digit of the highest bits that vary is histogrammed (2048 LDS bins); one wave
-//    scans the bins; the members of a threshold bin with at most 512 of them are
-//    ranked by (key desc, order asc), one per thread, otherwise the next digit is
+//    scans the bins; the members of a threshold bin with at most 64 of them are
+//    ranked by (key desc, order asc) by one wave, otherwise the next digit is
 //    examined.
 //  - output: per-chunk ballots give each item its rank among the selected items, so
 //    positions come out ascending without sorting.
@@ -32,8 +32,12 @@ constexpr int NW = NT / kWave;
 #ifndef CSA2_SEL_DIGIT
 #define CSA2_SEL_DIGIT 11
 #endif
+// A threshold bin of at most CSA2_SEL_MEMMAX keys is resolved from its members; larger
+// bins take another histogram pass over the next digit.  64 (every resolve a direct rank
+// by one wave) measured fastest: one-row step 35.8 -> 35.4 us against 256 (bins of 65-256
+// keys resolved by a radix-4 descent); 11-bit digits beat 10 and 12.
 #ifndef CSA2_SEL_MEMMAX
-#define CSA2_SEL_MEMMAX 256
+#define CSA2_SEL_MEMMAX 64
 #endif
 constexpr int kDigit = CSA2_SEL_DIGIT;                       // key bits ranked per histogram pass
 constexpr int kBins = 1 << kDigit;
