@@ -45,7 +45,13 @@ static_assert(kBins >= 4 * kWave && kBins <= kWave * kWave, "bins per lane: 4 ..
 constexpr int kMemMax = CSA2_SEL_MEMMAX;                     // bin members resolved directly
 constexpr int kMaxCand = (CSA2_KEEP_MAX + 1) * CSA2_BLOCK;   // 8256 candidate slots
 constexpr int kLdsBlocks = 16384;                            // block keys held in LDS
-constexpr int kGB = 16;                                      // gather batch per thread
+// Gather batch per thread: 9 covers a fine stage of up to 72 kept blocks (4,608
+// candidates) in one round of loads.  Every load of a batch is issued (clamped), so a
+// larger batch only adds loads: 16 made the one-row step 1.5 us slower.
+#ifndef CSA2_SEL_GATHER_BATCH
+#define CSA2_SEL_GATHER_BATCH 9
+#endif
+constexpr int kGB = CSA2_SEL_GATHER_BATCH;                   // gather batch per thread
 static_assert(kMaxCand >= CSA2_TOPK_ALL_MAX, "candidate buffer");
 static_assert(kLdsBlocks >= kMaxCand, "shared key buffer");
 static_assert(kLdsBlocks >= kSelSliceCand && kSelSlice % kWave == 0, "sliced coarse stage buffers");
@@ -296,13 +302,13 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // address when !ok) and ok(i) tells whether item i < n exists; kGB independent loads in
 // flight per thread; kbuf is zero-padded to whole chunks.  Publishes the per-wave key
 // range and zeroes the first histogram buffer; the caller then needs one barrier.
-template <class ValidF, class LoadF>
+template <int GB = kGB, class ValidF, class LoadF>
 __device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShared& sh,
                        const float* pre = nullptr) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, cnt = 0u;
-  auto keys = [&](int base, const float (&v)[kGB], const bool (&ok)[kGB]) {
+  auto keys = [&](int base, const float (&v)[GB], const bool (&ok)[GB]) {
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
+    for (int u = 0; u < GB; ++u) {
       const int i = base + u * NT + (int)threadIdx.x;
       const uint32_t kk = score_key(v[u]) & (0u - (uint32_t)ok[u]);   // masked, not branched
       if (i < n) kbuf[i] = kk;
@@ -314,22 +320,22 @@ __device__ void gather(int n, ValidF valid, LoadF load, uint32_t* kbuf, SelShare
   };
   int base0 = 0;
   if (pre) {   // the first batch was loaded by the caller
-    float v[kGB];
-    bool ok[kGB];
+    float v[GB];
+    bool ok[GB];
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
+    for (int u = 0; u < GB; ++u) {
       const int i = u * NT + (int)threadIdx.x;
       ok[u] = (i < n) & valid(i);
       v[u] = pre[u];
     }
     keys(0, v, ok);
-    base0 = NT * kGB;
+    base0 = NT * GB;
   }
-  for (int base = base0; base < n; base += NT * kGB) {
-    float v[kGB];
-    bool ok[kGB];
+  for (int base = base0; base < n; base += NT * GB) {
+    float v[GB];
+    bool ok[GB];
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
+    for (int u = 0; u < GB; ++u) {
       const int i = base + u * NT + (int)threadIdx.x;
       ok[u] = (i < n) & valid(i);   // valid() must accept any i (clamped reads)
       v[u] = load(i, ok[u]);
@@ -355,11 +361,12 @@ __device__ __forceinline__ int row_blocks(const SelectArgs& a, int r, int64_t& n
 
 // First gather batch of row r's block scores, loaded before the row's offsets are known
 // (the loads are clamped to the row's blk_ld <= kLdsBlocks slots).
-__device__ __forceinline__ void prefetch_blocks(const SelectArgs& a, int r, float (&pre)[kGB]) {
+template <int GB>
+__device__ __forceinline__ void prefetch_blocks(const SelectArgs& a, int r, float (&pre)[GB]) {
   const float* bs = a.blk_scores + (int64_t)r * a.blk_ld;
   const int lim = (int)a.blk_ld - 1;
 #pragma unroll
-  for (int u = 0; u < kGB; ++u) pre[u] = bs[min(u * NT + (int)threadIdx.x, lim)];
+  for (int u = 0; u < GB; ++u) pre[u] = bs[min(u * NT + (int)threadIdx.x, lim)];
   // Keep the loads here, ahead of the offset loads' waits.
   asm volatile("" ::: "memory");
 }
@@ -367,7 +374,7 @@ __device__ __forceinline__ void prefetch_blocks(const SelectArgs& a, int r, floa
 // Coarse stage of row r: kept blocks (ascending) into sh.kl / sh.nk and, if given, the
 // global kept list.  BIG: blk_ld may exceed kLdsBlocks (rows with more blocks rank
 // straight from global memory); otherwise pre holds the first gather batch.
-template <bool BIG>
+template <bool BIG, int GB = kGB>
 __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32_t* kbuf, const float* pre) {
   const float* bs = a.blk_scores + (int64_t)r * a.blk_ld;
   int32_t* kout = a.kept ? a.kept + (int64_t)r * a.kept_ld : nullptr;
@@ -383,8 +390,8 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
     // loads clamped to them, so they need not wait for the request's offsets; items at
     // or past nb are masked to empty keys.
     const int lim = (int)(a.blk_ld < kLdsBlocks ? a.blk_ld : kLdsBlocks);
-    gather(lim, [&](int i) { return i < nb; }, [&](int i, bool) { return bs[min(i, lim - 1)]; }, kbuf, sh,
-           BIG ? nullptr : pre);
+    gather<GB>(lim, [&](int i) { return i < nb; }, [&](int i, bool) { return bs[min(i, lim - 1)]; }, kbuf, sh,
+               BIG ? nullptr : pre);
     __syncthreads();
     cnt = sel_top([&](int i) { return kbuf[i]; }, nb, valid_count(sh), a.n_keep, sh, emit);
   } else {
@@ -438,12 +445,13 @@ __device__ void coarse_cand(const SelectArgs& a, int r, int nb, SelShared& sh, u
     if (kout) kout[pos] = blk;
     if (blk == nb - 1) sh.flag = 1;
   };
-  // gather() evaluates valid(i) for every i of its last whole batch (up to NT * kGB - 1,
-  // past `items`), so the slice index is clamped to the row's slices: cand_n is the
+  // gather() evaluates valid(i) for every i of its last whole batch (up to
+  // kSelSliceCand - 1, past `items`), so the slice index is clamped to the row's slices: cand_n is the
   // last buffer of the decode workspace and must not be read past its end.
   const int last_slice = a.n_slices - 1;
-  gather(items, [&](int i) { return i % K < cn[min(i / K, last_slice)]; },
-         [&](int i, bool ok) { return cs[ok ? i : 0]; }, kbuf, sh);
+  static_assert(kSelSliceCand % NT == 0, "candidate gather: one batch of whole rows");
+  gather<kSelSliceCand / NT>(items, [&](int i) { return i % K < cn[min(i / K, last_slice)]; },
+                             [&](int i, bool ok) { return cs[ok ? i : 0]; }, kbuf, sh);
   __syncthreads();
   int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), K, sh, emit);
   __syncthreads();
@@ -524,7 +532,7 @@ __global__ __launch_bounds__(NT) void k_block_select(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
   float pre[kGB];
-  if (!BIG) prefetch_blocks(a, blockIdx.x, pre);
+  if (!BIG) prefetch_blocks<kGB>(a, blockIdx.x, pre);
   int64_t n, e0;
   const int nb = row_blocks<PAGED>(a, blockIdx.x, n, e0);
   coarse<BIG>(a, blockIdx.x, nb, sh, kbuf, pre);
@@ -565,7 +573,8 @@ __global__ __launch_bounds__(NT) void k_block_slices(SelectArgs a) {
     return;
   }
   const float* bs = a.blk_scores + (int64_t)r * a.blk_ld + j0;
-  gather(items, [](int) { return true; }, [&](int i, bool ok) { return bs[ok ? i : 0]; }, kbuf, sh);
+  static_assert(kSelSlice % NT == 0, "slice gather: one batch of whole rows");
+  gather<kSelSlice / NT>(items, [](int) { return true; }, [&](int i, bool ok) { return bs[ok ? i : 0]; }, kbuf, sh);
   __syncthreads();
   const int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), a.n_keep, sh, [&](int pos, int i) {
     a.cand_blk[slot + pos] = j0 + i;
@@ -576,20 +585,23 @@ __global__ __launch_bounds__(NT) void k_block_slices(SelectArgs a) {
 
 // Both stages for one row; the block keys and the candidate keys share one LDS buffer.
 // CMODE 0: all blocks ranked from LDS (first batch prefetched); 1: rows may have more
-// blocks than LDS holds; 2: the sliced coarse stage's candidates.
+// blocks than LDS holds; 2: the sliced coarse stage's candidates; 3: as 0 for rows of at
+// most 2 x NT block slots, whose whole gather is two loads per thread (a batch sized for
+// more blocks would issue loads that only repeat the last slot).
 template <bool PAGED, int CMODE>
 __global__ __launch_bounds__(NT) void k_select_fused(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
+  constexpr int GBC = CMODE == 3 ? 2 : kGB;
   const int r = blockIdx.x;
-  float pre[kGB];
-  if (CMODE == 0) prefetch_blocks(a, r, pre);
+  float pre[GBC];
+  if (CMODE == 0 || CMODE == 3) prefetch_blocks(a, r, pre);
   int64_t n, e0;
   const int nb = row_blocks<PAGED>(a, r, n, e0);
   if (CMODE == 2)
     coarse_cand(a, r, nb, sh, kbuf);
   else
-    coarse<CMODE == 1>(a, r, nb, sh, kbuf, pre);
+    coarse<CMODE == 1, GBC>(a, r, nb, sh, kbuf, pre);
   __syncthreads();
   fine<PAGED>(a, r, n, e0, sh.nk, false, sh, kbuf);
 }
@@ -619,15 +631,20 @@ hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st) {
 
 hipError_t launch_select_fused(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : 0);
+#ifndef CSA2_SEL_SMALL_ROWS
+#define CSA2_SEL_SMALL_ROWS 1
+#endif
+  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : (CSA2_SEL_SMALL_ROWS && a.blk_ld <= 2 * NT ? 3 : 0));
   const dim3 grid(a.g.R), block(NT);
   if (a.g.page_table) {
     if (mode == 2) k_select_fused<true, 2><<<grid, block, 0, st>>>(a);
     else if (mode == 1) k_select_fused<true, 1><<<grid, block, 0, st>>>(a);
+    else if (mode == 3) k_select_fused<true, 3><<<grid, block, 0, st>>>(a);
     else k_select_fused<true, 0><<<grid, block, 0, st>>>(a);
   } else {
     if (mode == 2) k_select_fused<false, 2><<<grid, block, 0, st>>>(a);
     else if (mode == 1) k_select_fused<false, 1><<<grid, block, 0, st>>>(a);
+    else if (mode == 3) k_select_fused<false, 3><<<grid, block, 0, st>>>(a);
     else k_select_fused<false, 0><<<grid, block, 0, st>>>(a);
   }
   return hipGetLastError();
