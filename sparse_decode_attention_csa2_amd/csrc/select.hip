@@ -98,6 +98,11 @@ __device__ __forceinline__ int valid_count(const SelShared& sh) {
   return c;
 }
 
+// Score of a key (inverse of score_key for non-zero keys).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // k-th largest key among the valid items (1 <= k < valid count): T and n_gt = number of
 // keys > T.  key(i), defined for every i in the whole chunks covering n, returns 0 for
 // an empty item.  Expects the per-wave key ranges in sh.red and sh.hist[0] zeroed,
@@ -112,10 +117,120 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     lo = min(lo, sh.red[2 * w]);
     hi = max(hi, sh.red[2 * w + 1]);
   }
+
+  // Wave 0: the bin of hist holding the rem-th largest key (bins ascend with the keys)
+  // into sh.digit, the keys in higher bins into sh.above, the bin's count into sh.m.
+  auto find_bin = [&](const uint32_t* hist, int rem) {
+    // Lane l owns the kPer bins below kBins - kPer * l (highest first); find the bin
+    // holding the rem-th key.
+    constexpr int kPer = kBins / kWave;
+    const uint32_t* hb = hist + kBins - kPer * (lane + 1);
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hb + 4 * q);
+      tot += v[0] + v[1] + v[2] + v[3];
+    }
+    const uint32_t before = wave_incl_scan(tot) - tot;
+    // The lane whose kPer bins hold the rem-th key; its bins are then examined by
+    // lanes 0 .. kPer-1 in parallel (lane x takes the x-th bin in descending order).
+    const uint64_t owner = __ballot(before < (uint32_t)rem && before + tot >= (uint32_t)rem);
+    const int tl = owner ? (int)__builtin_ctzll(owner) : kWave - 1;
+    const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
+    const int x = lane & (kPer - 1);
+    const uint32_t bin = (uint32_t)(kBins - kPer * (tl + 1) + (kPer - 1 - x));
+    const uint32_t cnt = lane < kPer ? hist[bin] : 0u;
+    const uint32_t incl = tb + wave_incl_scan(cnt);
+    const uint64_t hit = __ballot(lane < kPer && incl >= (uint32_t)rem);
+    if (lane == (int)__builtin_ctzll(hit)) {
+      sh.digit = bin;
+      sh.above = incl - cnt;
+      sh.m = (int)cnt;
+    }
+  };
+
+  // Members of the threshold bin (member(key) true) into sh.mkey / sh.mcnt; the caller
+  // then needs one barrier.
+  auto collect = [&](auto member) {
+#pragma unroll 4
+    for (int c = c0; c < c1; ++c) {
+      const int i = c * kWave + lane;
+      const uint32_t kk = key(i);
+      if (kk && member(kk)) {
+        const int slot = atomicAdd(&sh.mcnt, 1);
+        sh.mkey[slot] = kk;
+      }
+    }
+  };
+
+  // Wave 0, at most 64 members: lane i ranks member i against all of them (keys > and
+  // ==); the rem-th largest is held by the lane with n_greater < rem <= n_greater +
+  // n_equal.
+  auto rank_members = [&](int rem, int above_total) {
+    const int m = __builtin_amdgcn_readfirstlane(sh.mcnt);
+    const uint32_t kk = lane < m ? sh.mkey[lane] : 0u;
+    uint32_t gt = 0u, eq = 0u;
+    for (int j = 0; j < m; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kk, j);
+      gt += kj > kk ? 1u : 0u;
+      eq += kj == kk ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(lane < m && gt < (uint32_t)rem && (uint32_t)rem <= gt + eq);
+    const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+    if (lane == src) {
+      sh.T = kk;
+      sh.n_gt = above_total + (int)gt;
+    }
+  };
+
+  // First pass: bins linear in the score between the smallest and the largest valid
+  // score.  The float keys' leading bits are mostly exponent, so an 11-bit digit of them
+  // puts a row's scores into a few dozen of the 2,048 bins and the threshold bin often
+  // holds over a hundred keys (one more histogram pass); bins linear in the value leave a
+  // few keys in it.  The bin is a non-decreasing function of the key (one rounding of
+  // s * scale + off, clamped), so bins ascend with the keys and the threshold bin's
+  // members are exactly the keys that map to it.  A bin of more than 64 keys, or a range
+  // that does not give finite bins, continues with the digits of the key bits.
+  int buf = 0;
+  {
+    const float slo = key_score(lo), shi = key_score(hi);
+    const float range = shi - slo;
+    const float scale = (float)kBins / range;
+    const float off = -slo * scale;
+    const bool lin_ok = range > 0.f && scale < __builtin_inff() && off < __builtin_inff() && off > -__builtin_inff();
+    if (lin_ok) {
+      auto lbin = [&](uint32_t kk) {
+        return (uint32_t)__builtin_amdgcn_fmed3f(__builtin_fmaf(key_score(kk), scale, off), 0.f, (float)(kBins - 1));
+      };
+      uint32_t* hist = sh.hist[0];
+#pragma unroll 4
+      for (int c = c0; c < c1; ++c) {
+        const uint32_t kk = key(c * kWave + lane);
+        if (kk) atomicAdd(&hist[lbin(kk)], 1u);
+      }
+      for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[1][i] = 0u;
+      if (threadIdx.x == 0) sh.mcnt = 0;
+      __syncthreads();
+      if (wave == 0) find_bin(hist, k);
+      __syncthreads();
+      if (sh.m <= kWave && sh.m <= kMemMax) {
+        const uint32_t d = sh.digit;
+        collect([&](uint32_t kk) { return lbin(kk) == d; });
+        __syncthreads();
+        if (wave == 0) rank_members(k - (int)sh.above, (int)sh.above);
+        __syncthreads();
+        T = sh.T;
+        n_gt = sh.n_gt;
+        return;
+      }
+      buf = 1;   // sh.hist[1] is zeroed
+    }
+  }
+
   const uint32_t span = hi - lo;
   int L = span ? 32 - __builtin_clz(span) : 0;   // bits of (key - lo) that vary
   uint32_t prefix = 0u;                           // (key - lo) >> L of the keys in play
-  int rem = k, above_total = 0, buf = 0;
+  int rem = k, above_total = 0;
   while (true) {
     const int shift = L > kDigit ? L - kDigit : 0;
     const uint32_t dmask = (1u << (L - shift)) - 1u;
@@ -129,34 +244,7 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[buf ^ 1][i] = 0u;
     if (threadIdx.x == 0) sh.mcnt = 0;
     __syncthreads();
-    if (wave == 0) {
-      // Lane l owns the kPer bins below kBins - kPer * l (highest first); find the bin
-      // holding the rem-th key.
-      constexpr int kPer = kBins / kWave;
-      const uint32_t* hb = hist + kBins - kPer * (lane + 1);
-      uint32_t tot = 0u;
-#pragma unroll
-      for (int q = 0; q < kPer / 4; ++q) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hb + 4 * q);
-        tot += v[0] + v[1] + v[2] + v[3];
-      }
-      const uint32_t before = wave_incl_scan(tot) - tot;
-      // The lane whose kPer bins hold the rem-th key; its bins are then examined by
-      // lanes 0 .. kPer-1 in parallel (lane x takes the x-th bin in descending order).
-      const uint64_t owner = __ballot(before < (uint32_t)rem && before + tot >= (uint32_t)rem);
-      const int tl = owner ? (int)__builtin_ctzll(owner) : kWave - 1;
-      const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
-      const int x = lane & (kPer - 1);
-      const uint32_t bin = (uint32_t)(kBins - kPer * (tl + 1) + (kPer - 1 - x));
-      const uint32_t cnt = lane < kPer ? hist[bin] : 0u;
-      const uint32_t incl = tb + wave_incl_scan(cnt);
-      const uint64_t hit = __ballot(lane < kPer && incl >= (uint32_t)rem);
-      if (lane == (int)__builtin_ctzll(hit)) {
-        sh.digit = bin;
-        sh.above = incl - cnt;
-        sh.m = (int)cnt;
-      }
-    }
+    if (wave == 0) find_bin(hist, rem);
     __syncthreads();
     const int m = sh.m;
     rem -= (int)sh.above;
@@ -173,33 +261,10 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
   }
   // Collect the bin's members; one wave then finds the rem-th largest member key and
   // counts the members above it.
-#pragma unroll 4
-  for (int c = c0; c < c1; ++c) {
-    const int i = c * kWave + lane;
-    const uint32_t kk = key(i);
-    if (kk && ((uint64_t)(kk - lo) >> L) == prefix) {
-      const int slot = atomicAdd(&sh.mcnt, 1);
-      sh.mkey[slot] = kk;
-    }
-  }
+  collect([&](uint32_t kk) { return ((uint64_t)(kk - lo) >> L) == prefix; });
   __syncthreads();
   if (wave == 0 && sh.mcnt <= kWave) {
-    // At most 64 members: lane i ranks member i against all of them (keys > and ==);
-    // the rem-th largest is held by the lane with n_greater < rem <= n_greater + n_equal.
-    const int m = __builtin_amdgcn_readfirstlane(sh.mcnt);
-    const uint32_t k = lane < m ? sh.mkey[lane] : 0u;
-    uint32_t gt = 0u, eq = 0u;
-    for (int j = 0; j < m; ++j) {
-      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)k, j);
-      gt += kj > k ? 1u : 0u;
-      eq += kj == k ? 1u : 0u;
-    }
-    const uint64_t hit = __ballot(lane < m && gt < (uint32_t)rem && (uint32_t)rem <= gt + eq);
-    const int src = hit ? (int)__builtin_ctzll(hit) : 0;
-    if (lane == src) {
-      sh.T = k;
-      sh.n_gt = above_total + (int)gt;
-    }
+    rank_members(rem, above_total);
   } else if (wave == 0) {
     // More members: descend over the bits below the bin's prefix two at a time; per
     // step, count the members at or above each of the three candidate extensions with
@@ -292,10 +357,6 @@ __device__ int sel_top(KeyF key, int n, int n_valid, int take, SelShared& sh, Em
   }
   sel_emit(key, n, T, take - n_gt, sh, emit);
   return take;
-}
-
-__device__ __forceinline__ float key_score(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // Gather item scores into kbuf as keys: load(i, ok) reads item i's score (a safe

@@ -202,6 +202,48 @@ def test_topk_exact_on_given_scores(csa2, k):
         assert np.array_equal(ss[r, :n_sel[r]], sc[r, ref])
 
 
+@pytest.mark.parametrize("k", [7, 512])
+def test_topk_exact_value_ranges(csa2, k):
+    # Score ranges that the select's first pass (bins linear in the score) cannot bin
+    # finely, so it must fall back to digits of the key bits, next to ones it can:
+    # one huge outlier, infinities, a range of a few denormals, scores one ulp apart,
+    # a heavy-tailed row with NaNs, and both signs.
+    _log(f"top-k value ranges: k {k}")
+    wl = make_workload("topkrange", 7, [64 * 66] * 6, rows_per_req=1, n_needles=0)
+    dw = upload(wl)
+    rng = np.random.default_rng(100 + k)
+    R, ld = wl.num_rows, wl.max_entries
+    sc = (rng.standard_normal((R, ld)) * 1e-3).astype(np.float32)
+    sc[0, 17] = 1e30
+    sc[1, rng.choice(ld, 40, replace=False)] = np.inf
+    sc[1, rng.choice(ld, 40, replace=False)] = -np.inf
+    sc[2] = rng.integers(1, 30, size=ld).astype(np.float32) * np.float32(1e-45)   # denormals
+    sc[3] = np.float32(1.0) + np.arange(ld, dtype=np.float32) * np.float32(2 ** -23)   # one ulp apart
+    rng.shuffle(sc[3])
+    sc[4] = rng.exponential(1.0, size=ld).astype(np.float32) ** 4
+    sc[4, rng.choice(ld, 100, replace=False)] = np.nan
+    sc[5] = rng.standard_normal(ld).astype(np.float32) * 100
+    kept_rows = []
+    for r in range(R):
+        nb = -(-wl.n_entries(int(wl.row_req[r])) // 64)
+        kept_rows.append(np.arange(nb))
+    kept = np.full((R, 66), -1, dtype=np.int32)
+    n_kept = np.zeros(R, dtype=np.int32)
+    for r, kk in enumerate(kept_rows):
+        kept[r, :kk.size] = kk
+        n_kept[r] = kk.size
+    sel, n_sel, ss = csa2.topk(dw.rg, torch.from_numpy(sc).cuda(), torch.from_numpy(kept).cuda(),
+                               torch.from_numpy(n_kept).cuda(), k=k, with_scores=True)
+    sel, n_sel, ss = sel.cpu().numpy(), n_sel.cpu().numpy(), ss.cpu().numpy()
+    for r in range(R):
+        b = int(wl.row_req[r])
+        cand = oracle.blocks_to_entries(kept_rows[r], wl.n_entries(b))
+        ref = oracle.top_k(cand, sc[r, cand].astype(np.float64), k)
+        assert n_sel[r] == ref.size, f"row {r}"
+        assert sel[r, :n_sel[r]].tolist() == ref.tolist(), f"row {r}"
+        assert np.array_equal(ss[r, :n_sel[r]], sc[r, ref])
+
+
 def test_topk_all_entries_mode(csa2):
     _log("top-k over all entries")
     wl = make_workload("topkall", 4, [8192, 513, 512, 3], rows_per_req=1, n_needles=0)
