@@ -32,10 +32,10 @@ constexpr int NW = NT / kWave;
 #ifndef CSA2_SEL_DIGIT
 #define CSA2_SEL_DIGIT 11
 #endif
-// A threshold bin of at most CSA2_SEL_MEMMAX keys is resolved from its members; larger
-// bins take another histogram pass over the next digit.  64 (every resolve a direct rank
-// by one wave) measured fastest: one-row step 35.8 -> 35.4 us against 256 (bins of 65-256
-// keys resolved by a radix-4 descent); 11-bit digits beat 10 and 12.
+// A threshold bin of at most CSA2_SEL_MEMMAX (<= 64) keys is resolved from its members
+// by one wave; larger bins take another histogram pass over the next digit.  64 measured
+// fastest: one-row step 35.8 -> 35.4 us against 256 (bins of 65-256 keys resolved by a
+// radix-4 descent); 11-bit digits beat 10 and 12.
 #ifndef CSA2_SEL_MEMMAX
 #define CSA2_SEL_MEMMAX 64
 #endif
@@ -43,6 +43,7 @@ constexpr int kDigit = CSA2_SEL_DIGIT;                       // key bits ranked 
 constexpr int kBins = 1 << kDigit;
 static_assert(kBins >= 4 * kWave && kBins <= kWave * kWave, "bins per lane: 4 .. 64");
 constexpr int kMemMax = CSA2_SEL_MEMMAX;                     // bin members resolved directly
+static_assert(kMemMax >= 1 && kMemMax <= 64, "members are ranked one per lane");
 constexpr int kMaxCand = (CSA2_KEEP_MAX + 1) * CSA2_BLOCK;   // 8256 candidate slots
 constexpr int kLdsBlocks = 16384;                            // block keys held in LDS
 // Gather batch per thread: 9 covers a fine stage of up to 72 kept blocks (4,608
@@ -62,6 +63,7 @@ struct SelShared {
   uint32_t cnt[NW];
   uint32_t wgt[NW], weq[NW];
   uint32_t mkey[kMemMax];
+  uint32_t mwave[kMemMax];            // wave that holds each member
   uint32_t digit, above;
   int32_t m, mcnt;
   uint32_t T;
@@ -106,9 +108,10 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // k-th largest key among the valid items (1 <= k < valid count): T and n_gt = number of
 // keys > T.  key(i), defined for every i in the whole chunks covering n, returns 0 for
 // an empty item.  Expects the per-wave key ranges in sh.red and sh.hist[0] zeroed,
-// both behind a barrier.
+// both behind a barrier.  Returns true when it has also left each wave's count of keys
+// > T and == T (over the wave's chunks) in sh.wgt / sh.weq, behind a barrier.
 template <class KeyF>
-__device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int& n_gt) {
+__device__ bool sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int& n_gt) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   int c0, c1;
   wave_chunks(n, c0, c1);
@@ -149,26 +152,37 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     }
   };
 
-  // Members of the threshold bin (member(key) true) into sh.mkey / sh.mcnt; the caller
-  // then needs one barrier.
-  auto collect = [&](auto member) {
+  // Members of the threshold bin (member(key) true) into sh.mkey / sh.mwave / sh.mcnt,
+  // and each wave's count of keys above the bin (above(key) true) into sh.wgt; the
+  // caller then needs one barrier.
+  auto collect = [&](auto member, auto above) {
+    uint32_t gtc = 0u;   // per lane: no cross-lane operation in the loop, so it unrolls
 #pragma unroll 4
     for (int c = c0; c < c1; ++c) {
       const int i = c * kWave + lane;
       const uint32_t kk = key(i);
+      gtc += (kk && above(kk)) ? 1u : 0u;
       if (kk && member(kk)) {
         const int slot = atomicAdd(&sh.mcnt, 1);
         sh.mkey[slot] = kk;
+        sh.mwave[slot] = (uint32_t)wave;
       }
+    }
+    gtc = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(gtc), kWave - 1);
+    if (lane == 0) {
+      sh.wgt[wave] = gtc;
+      sh.weq[wave] = 0u;
     }
   };
 
   // Wave 0, at most 64 members: lane i ranks member i against all of them (keys > and
   // ==); the rem-th largest is held by the lane with n_greater < rem <= n_greater +
-  // n_equal.
+  // n_equal.  Then each wave's members > T join its count of keys above the bin, and its
+  // members == T give its count of ties.
   auto rank_members = [&](int rem, int above_total) {
     const int m = __builtin_amdgcn_readfirstlane(sh.mcnt);
     const uint32_t kk = lane < m ? sh.mkey[lane] : 0u;
+    const uint32_t kw = lane < m ? sh.mwave[lane] : (uint32_t)NW;
     uint32_t gt = 0u, eq = 0u;
     for (int j = 0; j < m; ++j) {
       const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kk, j);
@@ -177,9 +191,12 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     }
     const uint64_t hit = __ballot(lane < m && gt < (uint32_t)rem && (uint32_t)rem <= gt + eq);
     const int src = hit ? (int)__builtin_ctzll(hit) : 0;
-    if (lane == src) {
-      sh.T = kk;
-      sh.n_gt = above_total + (int)gt;
+    const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
+    const uint32_t tg = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+    if (lane < m) atomicAdd(kk > t ? &sh.wgt[kw] : &sh.weq[kw], kk >= t ? 1u : 0u);
+    if (lane == 0) {
+      sh.T = t;
+      sh.n_gt = above_total + (int)tg;
     }
   };
 
@@ -213,15 +230,15 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
       __syncthreads();
       if (wave == 0) find_bin(hist, k);
       __syncthreads();
-      if (sh.m <= kWave && sh.m <= kMemMax) {
+      if (sh.m <= kMemMax) {
         const uint32_t d = sh.digit;
-        collect([&](uint32_t kk) { return lbin(kk) == d; });
+        collect([&](uint32_t kk) { return lbin(kk) == d; }, [&](uint32_t kk) { return lbin(kk) > d; });
         __syncthreads();
         if (wave == 0) rank_members(k - (int)sh.above, (int)sh.above);
         __syncthreads();
         T = sh.T;
         n_gt = sh.n_gt;
-        return;
+        return true;
       }
       buf = 1;   // sh.hist[1] is zeroed
     }
@@ -255,75 +272,44 @@ __device__ void sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     if (L == 0) {   // every key left is equal: the first rem of them by order
       T = lo + prefix;
       n_gt = above_total;
-      return;
+      return false;
     }
     if (m <= kMemMax) break;
   }
   // Collect the bin's members; one wave then finds the rem-th largest member key and
   // counts the members above it.
-  collect([&](uint32_t kk) { return ((uint64_t)(kk - lo) >> L) == prefix; });
+  collect([&](uint32_t kk) { return ((uint64_t)(kk - lo) >> L) == prefix; },
+          [&](uint32_t kk) { return ((uint64_t)(kk - lo) >> L) > prefix; });
   __syncthreads();
-  if (wave == 0 && sh.mcnt <= kWave) {
-    rank_members(rem, above_total);
-  } else if (wave == 0) {
-    // More members: descend over the bits below the bin's prefix two at a time; per
-    // step, count the members at or above each of the three candidate extensions with
-    // ballots and keep the largest extension that still has rem members at or above
-    // it.  Non-members hold 0, which no candidate (always >= 1) counts.
-    const int m = sh.mcnt;
-    uint32_t mk[kMemMax / kWave];
-#pragma unroll
-    for (int q = 0; q < kMemMax / kWave; ++q) {
-      const int i = q * kWave + lane;
-      mk[q] = i < m ? sh.mkey[i] - lo : 0u;
-    }
-    auto count_ge = [&](uint32_t cand) {
-      uint32_t c = 0u;
-#pragma unroll
-      for (int q = 0; q < kMemMax / kWave; ++q) c += __popcll(__ballot(mk[q] >= cand));
-      return c;
-    };
-    uint32_t t = prefix << L;   // candidate threshold (relative to lo)
-    int b = L;
-    while (b >= 2) {
-      b -= 2;
-      const uint32_t c1 = count_ge(t | (1u << b)), c2 = count_ge(t | (2u << b)), c3 = count_ge(t | (3u << b));
-      const uint32_t d = c3 >= (uint32_t)rem ? 3u : (c2 >= (uint32_t)rem ? 2u : (c1 >= (uint32_t)rem ? 1u : 0u));
-      t |= d << b;
-    }
-    if (b == 1 && count_ge(t | 1u) >= (uint32_t)rem) t |= 1u;
-    uint32_t gt = 0u;
-#pragma unroll
-    for (int q = 0; q < kMemMax / kWave; ++q) gt += __popcll(__ballot(mk[q] > t));
-    if (lane == 0) {
-      sh.T = t + lo;
-      sh.n_gt = above_total + (int)gt;
-    }
-  }
+  if (wave == 0) rank_members(rem, above_total);
   __syncthreads();
   T = sh.T;
   n_gt = sh.n_gt;
+  return true;
 }
 
 // Emit (output position, item) for every valid key > T and the first need_eq keys
-// == T, positions ascending with item order.  All threads must call it.
+// == T, positions ascending with item order.  counted: each wave's counts of keys > T
+// and == T are already in sh.wgt / sh.weq (behind a barrier).  All threads must call it.
 template <class KeyF, class EmitF>
-__device__ void sel_emit(KeyF key, int n, uint32_t T, int need_eq, SelShared& sh, EmitF emit) {
+__device__ void sel_emit(KeyF key, int n, uint32_t T, int need_eq, bool counted, SelShared& sh, EmitF emit) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   int c0, c1;
   wave_chunks(n, c0, c1);
-  uint32_t gtc = 0u, eqc = 0u;
+  if (!counted) {
+    uint32_t gtc = 0u, eqc = 0u;
 #pragma unroll 4
-  for (int c = c0; c < c1; ++c) {
-    const uint32_t kk = key(c * kWave + lane);
-    gtc += __popcll(__ballot(kk > T));
-    eqc += __popcll(__ballot(kk && kk == T));
+    for (int c = c0; c < c1; ++c) {
+      const uint32_t kk = key(c * kWave + lane);
+      gtc += __popcll(__ballot(kk > T));
+      eqc += __popcll(__ballot(kk && kk == T));
+    }
+    if (lane == 0) {
+      sh.wgt[wave] = gtc;
+      sh.weq[wave] = eqc;
+    }
+    __syncthreads();
   }
-  if (lane == 0) {
-    sh.wgt[wave] = gtc;
-    sh.weq[wave] = eqc;
-  }
-  __syncthreads();
   uint32_t gb = 0u, eb = 0u;
   for (int w = 0; w < wave; ++w) {
     gb += sh.wgt[w];
@@ -350,12 +336,13 @@ template <class KeyF, class EmitF>
 __device__ int sel_top(KeyF key, int n, int n_valid, int take, SelShared& sh, EmitF emit) {
   uint32_t T = 0u;
   int n_gt = 0;
+  bool counted = false;
   if (n_valid > take) {
-    sel_kth(key, n, take, sh, T, n_gt);
+    counted = sel_kth(key, n, take, sh, T, n_gt);
   } else {
     take = n_valid;
   }
-  sel_emit(key, n, T, take - n_gt, sh, emit);
+  sel_emit(key, n, T, take - n_gt, counted, sh, emit);
   return take;
 }
 
