@@ -288,11 +288,14 @@ __device__ bool sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
   return true;
 }
 
-// Emit (output position, item) for every valid key > T and the first need_eq keys
-// == T, positions ascending with item order.  counted: each wave's counts of keys > T
-// and == T are already in sh.wgt / sh.weq (behind a barrier).  All threads must call it.
-template <class KeyF, class EmitF>
-__device__ void sel_emit(KeyF key, int n, uint32_t T, int need_eq, bool counted, SelShared& sh, EmitF emit) {
+// Emit (output position, item, key, aux(item)) for every valid key > T and the first
+// need_eq keys == T, positions ascending with item order.  aux(i) (any i in the whole
+// chunks covering n) is read with the key, ahead of the test, so the emit waits on no
+// read of its own.  counted: each wave's counts of keys > T and == T are already in
+// sh.wgt / sh.weq (behind a barrier).  All threads must call it.
+template <class KeyF, class AuxF, class EmitF>
+__device__ void sel_emit(KeyF key, int n, uint32_t T, int need_eq, bool counted, SelShared& sh, AuxF aux,
+                         EmitF emit) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   int c0, c1;
   wave_chunks(n, c0, c1);
@@ -319,21 +322,26 @@ __device__ void sel_emit(KeyF key, int n, uint32_t T, int need_eq, bool counted,
   for (int c = c0; c < c1; ++c) {
     const int i = c * kWave + lane;
     const uint32_t kk = key(i);
+    const auto ax = aux(i);
     const bool g = kk > T, e = kk && kk == T;
     const uint64_t bg = __ballot(g), be = __ballot(e);
     const uint32_t gbl = gb + __popcll(bg & below), ebl = eb + __popcll(be & below);
-    if (g)
-      emit((int)(gbl + min(ebl, (uint32_t)need_eq)), i);
-    else if (e && ebl < (uint32_t)need_eq)
-      emit((int)(gbl + ebl), i);
+    // An item > T follows the ties taken before it; a tie is taken while ebl < need_eq,
+    // where min(ebl, need_eq) = ebl: one position formula for both.
+    if (g || (e && ebl < (uint32_t)need_eq)) emit((int)(gbl + min(ebl, (uint32_t)need_eq)), i, kk, ax);
     gb += __popcll(bg);
     eb += __popcll(be);
   }
 }
 
+// Item aux for emits that need none.
+struct NoAux {
+  __device__ int operator()(int) const { return 0; }
+};
+
 // The `take` best of n items (everything valid when n_valid <= take); returns the count.
-template <class KeyF, class EmitF>
-__device__ int sel_top(KeyF key, int n, int n_valid, int take, SelShared& sh, EmitF emit) {
+template <class KeyF, class AuxF, class EmitF>
+__device__ int sel_top(KeyF key, int n, int n_valid, int take, SelShared& sh, AuxF aux, EmitF emit) {
   uint32_t T = 0u;
   int n_gt = 0;
   bool counted = false;
@@ -342,7 +350,7 @@ __device__ int sel_top(KeyF key, int n, int n_valid, int take, SelShared& sh, Em
   } else {
     take = n_valid;
   }
-  sel_emit(key, n, T, take - n_gt, counted, sh, emit);
+  sel_emit(key, n, T, take - n_gt, counted, sh, aux, emit);
   return take;
 }
 
@@ -427,7 +435,7 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
   const float* bs = a.blk_scores + (int64_t)r * a.blk_ld;
   int32_t* kout = a.kept ? a.kept + (int64_t)r * a.kept_ld : nullptr;
   if (threadIdx.x == 0) sh.flag = 0;
-  auto emit = [&](int pos, int i) {
+  auto emit = [&](int pos, int i, uint32_t, int) {
     sh.kl[pos] = i;
     if (kout) kout[pos] = i;
     if (i == nb - 1) sh.flag = 1;
@@ -441,7 +449,7 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
     gather<GB>(lim, [&](int i) { return i < nb; }, [&](int i, bool) { return bs[min(i, lim - 1)]; }, kbuf, sh,
                BIG ? nullptr : pre);
     __syncthreads();
-    cnt = sel_top([&](int i) { return kbuf[i]; }, nb, valid_count(sh), a.n_keep, sh, emit);
+    cnt = sel_top([&](int i) { return kbuf[i]; }, nb, valid_count(sh), a.n_keep, sh, NoAux(), emit);
   } else {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0u;
     for (int i = threadIdx.x; i < nb; i += NT) {
@@ -457,7 +465,7 @@ __device__ void coarse(const SelectArgs& a, int r, int nb, SelShared& sh, uint32
       const float v = bs[i < nb ? i : 0];
       return i < nb ? score_key(v) : 0u;
     };
-    cnt = sel_top(gkey, nb, valid_count(sh), a.n_keep, sh, emit);
+    cnt = sel_top(gkey, nb, valid_count(sh), a.n_keep, sh, NoAux(), emit);
   }
   __syncthreads();
   // The newest block joins if the ranking left it out (it is the largest index, so the
@@ -487,7 +495,7 @@ __device__ void coarse_cand(const SelectArgs& a, int r, int nb, SelShared& sh, u
   const int32_t* cb = a.cand_blk + (int64_t)r * items;
   const int32_t* cn = a.cand_n + (int64_t)r * a.n_slices;
   if (threadIdx.x == 0) sh.flag = 0;
-  auto emit = [&](int pos, int i) {
+  auto emit = [&](int pos, int i, uint32_t, int) {
     const int blk = cb[i];
     sh.kl[pos] = blk;
     if (kout) kout[pos] = blk;
@@ -501,7 +509,7 @@ __device__ void coarse_cand(const SelectArgs& a, int r, int nb, SelShared& sh, u
   gather<kSelSliceCand / NT>(items, [&](int i) { return i % K < cn[min(i / K, last_slice)]; },
                              [&](int i, bool ok) { return cs[ok ? i : 0]; }, kbuf, sh);
   __syncthreads();
-  int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), K, sh, emit);
+  int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), K, sh, NoAux(), emit);
   __syncthreads();
   if (nb > 0 && a.keep_newest && sh.flag == 0) {
     if (threadIdx.x == 0) {
@@ -529,7 +537,6 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int64_t e0, int nk, 
   const int k = a.k;
   int32_t* sel = a.sel + (int64_t)r * k;
   float* ss = a.sel_score ? a.sel_score + (int64_t)r * k : nullptr;
-  auto pos_of = [&](int i) { return (int64_t)sh.kl[i / CSA2_BLOCK] * CSA2_BLOCK + (i % CSA2_BLOCK); };
   const int nk_c = nk > 0 ? nk : 1;   // slot index clamp for unconditional reads
   // Pool rows of the picks (attention over paged pools): thread s looks up the page of
   // kept block s (nk <= 129 < NT) once, with its load in flight together with the
@@ -562,10 +569,18 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int64_t e0, int nk, 
   }
   if (PAGED && rows && (int)threadIdx.x < nk) sh.kpage[threadIdx.x] = kpage;
   __syncthreads();
-  const int take = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), k, sh, [&](int pos, int i) {
-    sel[pos] = all_entries ? i : (int32_t)pos_of(i);
-    if (ss) ss[pos] = key_score(kbuf[i]);
-    if (rows) rows[pos] = PAGED ? sh.kpage[i / CSA2_BLOCK] + (i % CSA2_BLOCK) : (int32_t)(e0 + pos_of(i));
+  // aux of item i: its kept block's first position and, over paged pools, the block's
+  // first pool row.
+  auto aux = [&](int i) {
+    const int sl = min(i / CSA2_BLOCK, nk_c - 1);
+    return make_int2(sh.kl[sl] * CSA2_BLOCK, PAGED ? sh.kpage[sl] : 0);
+  };
+  const int take = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), k, sh, aux,
+                           [&](int pos, int i, uint32_t kk, int2 ax) {
+    const int j = i % CSA2_BLOCK;
+    sel[pos] = all_entries ? i : ax.x + j;
+    if (ss) ss[pos] = key_score(kk);
+    if (rows) rows[pos] = PAGED ? ax.y + j : (int32_t)(e0 + ax.x + j);
   });
   for (int i = take + threadIdx.x; i < k; i += NT) {
     sel[i] = -1;
@@ -624,9 +639,10 @@ __global__ __launch_bounds__(NT) void k_block_slices(SelectArgs a) {
   static_assert(kSelSlice % NT == 0, "slice gather: one batch of whole rows");
   gather<kSelSlice / NT>(items, [](int) { return true; }, [&](int i, bool ok) { return bs[ok ? i : 0]; }, kbuf, sh);
   __syncthreads();
-  const int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), a.n_keep, sh, [&](int pos, int i) {
+  const int cnt = sel_top([&](int i) { return kbuf[i]; }, items, valid_count(sh), a.n_keep, sh, NoAux(),
+                          [&](int pos, int i, uint32_t kk, int) {
     a.cand_blk[slot + pos] = j0 + i;
-    a.cand_sc[slot + pos] = key_score(kbuf[i]);
+    a.cand_sc[slot + pos] = key_score(kk);
   });
   if (threadIdx.x == 0) a.cand_n[(int64_t)r * a.n_slices + s] = cnt;
 }
