@@ -163,7 +163,7 @@ __device__ bool sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
       const uint32_t kk = key(i);
       gtc += (kk && above(kk)) ? 1u : 0u;
       if (kk && member(kk)) {
-        const int slot = atomicAdd(&sh.mcnt, 1);
+        const int slot = min(atomicAdd(&sh.mcnt, 1), kMemMax - 1);   // < m <= kMemMax by construction
         sh.mkey[slot] = kk;
         sh.mwave[slot] = (uint32_t)wave;
       }
@@ -223,7 +223,7 @@ __device__ bool sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
 #pragma unroll 4
       for (int c = c0; c < c1; ++c) {
         const uint32_t kk = key(c * kWave + lane);
-        if (kk) atomicAdd(&hist[lbin(kk)], 1u);
+        atomicAdd(&hist[lbin(kk) & (kBins - 1)], kk ? 1u : 0u);   // unconditional: no branch per key
       }
       for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[1][i] = 0u;
       if (threadIdx.x == 0) sh.mcnt = 0;
@@ -256,7 +256,7 @@ __device__ bool sel_kth(KeyF key, int n, int k, SelShared& sh, uint32_t& T, int&
     for (int c = c0; c < c1; ++c) {
       const uint32_t kk = key(c * kWave + lane);
       const uint32_t v = kk - lo;
-      if (kk && ((uint64_t)v >> L) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1u);
+      atomicAdd(&hist[(v >> shift) & dmask], (kk && ((uint64_t)v >> L) == prefix) ? 1u : 0u);
     }
     for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[buf ^ 1][i] = 0u;
     if (threadIdx.x == 0) sh.mcnt = 0;
