@@ -140,7 +140,14 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 // given and P as exact-to-2^-17 bf16 hi + lo parts.
 // HALF: the plan ends some splits with a half-full tile (split_keys not a multiple of
 // the tile), so tiles check for it; other plans get no trace of that path.
-template <bool MX, bool ROWS, bool HALF>
+// HS (launches with few workgroups, such as one row's 10 splits): a split's heads are
+// spread over four workgroups, one per head group (blockIdx.x = 4 split + hg).  Wave
+// (kb, dh) = (wave % 4, wave / 4) then contracts key block kb over dims 256dh.. for
+// S^T, every wave reads the whole 64-key S^T of the head group back from LDS, and wave
+// w owns dims 64w .. 64w+63 of O.  Every product and sum is the one the full workgroup
+// makes, in the same order, so the results are identical; each workgroup has a quarter
+// of the MFMA and LDS work per tile.
+template <bool MX, bool ROWS, bool HALF, bool HS = false>
 __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   constexpr int TK = kAttnTileKeys;   // 64
   constexpr int KB = TK / 32;         // 32-key groups
@@ -150,9 +157,12 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   __shared__ float ksc[TK];
   __shared__ int kval[TK];
 
-  const int r = blockIdx.y, split = blockIdx.x;
+  static_assert(!(HS && HALF), "head-split launches plan whole tiles");
+  constexpr int NO = HS ? 4 : 16;     // 16-dim O tiles per wave
+  const int r = blockIdx.y, split = HS ? (int)(blockIdx.x >> 2) : (int)blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, g = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), hg = wave & 3, dh = wave >> 2;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), dh = wave >> 2;
+  const int hg = HS ? (int)(blockIdx.x & 3) : (wave & 3);
   const int h = hg * 16 + ln;
   const int k_begin = split * a.split_keys;
 
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   const int n_keys = rk.n_main + rk.n_swa;
 
   if (n_keys == 0) {
-    if (split == 0) {
+    if (blockIdx.x == 0) {
       for (int i = tid; i < CSA2_HEADS * CSA2_D; i += 512) a.out[(int64_t)r * CSA2_HEADS * CSA2_D + i] = 0.f;
       if (tid < CSA2_HEADS) a.lse[(int64_t)r * CSA2_HEADS + tid] = -INFINITY;
     }
@@ -195,9 +205,9 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   if (k_begin >= n_keys) return;
   const int k_end = min(n_keys, k_begin + a.split_keys);
 
-  f32x4_t o[16];
+  f32x4_t o[NO];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NO; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.q);   // any readable 16-B aligned bytes
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 
   // Transposed-read offsets (elements): lane (g, i = 4k + q) points at key 4g + k of a
   // 16-key half and dims 4q .. 4q+3 of a 16-dim tile.
-  const int tr_off = (4 * g + (ln >> 2)) * KLS + 256 * dh + 4 * (ln & 3);
+  const int tr_off = (4 * g + (ln >> 2)) * KLS + (HS ? 64 * wave : 256 * dh) + 4 * (ln & 3);
 
   for (int kt = k_begin; kt < k_end; kt += TK) {
 #pragma unroll
@@ -269,7 +279,19 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     f32x4_t s[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (half) {
+    if constexpr (HS) {
+      // This wave's key block over its 256 dims; all eight partial blocks meet in LDS.
+      const int kb = wave & 3;
+      f32x4_t sk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8_t ak =
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * kb + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+        sk = mfma16x16x32(ak, qb[st], sk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sx[wave][i][lane] = sk[i];
+    } else if (half) {
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
 #pragma unroll
@@ -291,15 +313,23 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
       }
     }
     // The two dim halves of a head group meet in LDS.
+    if constexpr (HS) {
+      __syncthreads();
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sx[wave][4 * b + i][lane] = s[b][i];
-    __syncthreads();
+        for (int i = 0; i < 4; ++i) s[b][i] = Sx[b][i][lane] + Sx[b + 4][i][lane];
+    } else {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[b][i] += Sx[wave ^ 4][4 * b + i][lane];
+        for (int i = 0; i < 4; ++i) Sx[wave][4 * b + i][lane] = s[b][i];
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[b][i] += Sx[wave ^ 4][4 * b + i][lane];
+    }
 
     // Lane holds keys 16b + 4g + i for head h (the same values in both waves of the
     // head group: a + b == b + a).
@@ -346,7 +376,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     // Rescale the accumulators only when a head's running maximum moved.
     if (__ballot(m_new != m_run && m_run != -INFINITY)) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) o[t] *= alpha;
+      for (int t = 0; t < NO; ++t) o[t] *= alpha;
     }
     m_run = m_new;
     if (more) load_keys(kt + TK);
@@ -358,7 +388,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     for (int c = 0; c < KB; ++c) {
       if (half && c > 0) break;   // uniform: the second 32-key group is empty
 #pragma unroll
-      for (int t0 = 0; t0 < 16; t0 += 4) {
+      for (int t0 = 0; t0 < NO; t0 += 4) {
         bf16x8_t av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -379,22 +409,26 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   }
 
   const float l_tot = xor32_add(xor16_add(l_run));
-  // Lane holds O^T[256dh + 16t + 4g + i][h].
+  // Lane holds O^T[d0 + 16t + 4g + i][h] with d0 = 256dh (HS: 64 wave).
+  const int d0 = HS ? 64 * wave : 256 * dh;
+  const bool stat_writer = g == 0 && (HS ? wave == 0 : dh == 0);
   if (a.splits == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + 256 * dh + 4 * g;
+    float* op = a.out + ((int64_t)r * CSA2_HEADS + h) * CSA2_D + d0 + 4 * g;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4_t*>(op + 16 * t) = o[t] * inv;
-    if (g == 0 && dh == 0)
+    for (int t = 0; t < NO; ++t) *reinterpret_cast<f32x4_t*>(op + 16 * t) = o[t] * inv;
+    if (stat_writer)
       a.lse[(int64_t)r * CSA2_HEADS + h] = (m_run == -INFINITY) ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
   } else {
-    // Partials keep the accumulator fragment layout, [split][wave][t][lane][4], so every
-    // store instruction writes 1 KB of contiguous memory.
+    // Partials keep the accumulator fragment layout, [split][hg + 4 dh][t][lane][4]
+    // (dims 256dh + 16t), so every store instruction writes 1 KB of contiguous memory.
     const int64_t ps = (int64_t)r * a.splits + split;
-    float* op = a.opart + ((ps * 8 + wave) * 16) * 256 + 4 * lane;
+    const int slot = HS ? hg + 4 * (wave >> 2) : wave;
+    const int t0 = HS ? 4 * (wave & 3) : 0;
+    float* op = a.opart + ((ps * 8 + slot) * 16 + t0) * 256 + 4 * lane;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4_t*>(op + 256 * t) = o[t];
-    if (g == 0 && dh == 0) {
+    for (int t = 0; t < NO; ++t) *reinterpret_cast<f32x4_t*>(op + 256 * t) = o[t];
+    if (stat_writer) {
       a.mpart[ps * CSA2_HEADS + h] = m_run;
       a.lpart[ps * CSA2_HEADS + h] = l_tot;
     }
@@ -501,28 +535,36 @@ size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
   return parts * CSA2_D * sizeof(float) + 2 * parts * sizeof(float) + 3 * 256;
 }
 
-template <bool HALF>
+template <bool HALF, bool HS>
 static void launch_attn_variant(const AttnArgs& a, dim3 grid, hipStream_t st) {
   if (a.qp_route == CSA2_QP_MXFP8) {
     if (a.sel_rows)
-      k_attn<true, true, HALF><<<grid, dim3(512), 0, st>>>(a);
+      k_attn<true, true, HALF, HS><<<grid, dim3(512), 0, st>>>(a);
     else
-      k_attn<true, false, HALF><<<grid, dim3(512), 0, st>>>(a);
+      k_attn<true, false, HALF, HS><<<grid, dim3(512), 0, st>>>(a);
   } else {
     if (a.sel_rows)
-      k_attn<false, true, HALF><<<grid, dim3(512), 0, st>>>(a);
+      k_attn<false, true, HALF, HS><<<grid, dim3(512), 0, st>>>(a);
     else
-      k_attn<false, false, HALF><<<grid, dim3(512), 0, st>>>(a);
+      k_attn<false, false, HALF, HS><<<grid, dim3(512), 0, st>>>(a);
   }
 }
 
+// Head-split launches while four workgroups per split still fit one per CU.
+#ifndef CSA2_ATTN_HS
+#define CSA2_ATTN_HS 1
+#endif
+
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  const dim3 grid(a.splits, a.g.R);
-  if (a.split_keys % kAttnTileKeys != 0)
-    launch_attn_variant<true>(a, grid, st);
+  const bool half = a.split_keys % kAttnTileKeys != 0;
+  const bool hs = CSA2_ATTN_HS && !half && (int64_t)a.g.R * a.splits * 4 <= CSA2_ATTN_TARGET_WGS;
+  if (hs)
+    launch_attn_variant<false, true>(a, dim3(a.splits * 4, a.g.R), st);
+  else if (half)
+    launch_attn_variant<true, false>(a, dim3(a.splits, a.g.R), st);
   else
-    launch_attn_variant<false>(a, grid, st);
+    launch_attn_variant<false, false>(a, dim3(a.splits, a.g.R), st);
   return hipGetLastError();
 }
 

@@ -97,6 +97,20 @@ def test_mx_route_decode_matches_oracle(csa2, cfg):
     judge_mx(wl, got, rows=range(0, wl.num_rows, 5))
 
 
+@pytest.mark.parametrize("cfg, rows", [(1, None), (5, [0, 21, 42, 63])])
+def test_mx_route_full_size_matches_oracle(csa2, cfg, rows):
+    # The MXFP8 route at the sizes bench.py times it (one 128K row; sampled rows of the
+    # 64 x 128K batch): same selections as the BF16 route, attention within the oracle's
+    # bound for the route.
+    wl = make_config(cfg)
+    _log(f"config {cfg} ({wl.name}) MXFP8 route, full size")
+    got = run_decode(csa2, wl, csa2.QP_MXFP8)
+    ref = run_decode(csa2, wl, csa2.QP_BF16)
+    for key in ("sel", "n_sel", "kept", "n_kept"):
+        assert np.array_equal(got[key], ref[key]), key
+    judge_mx(wl, got, rows=rows)
+
+
 def test_mx_route_edge_and_paged(csa2):
     lens = [0, 1, 63, 64, 65, 511, 513, 64 * 65 + 63, 20000]
     swa = [0, 1, 128, 5, 0, 128, 77, 128, 128]

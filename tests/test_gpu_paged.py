@@ -192,6 +192,25 @@ def test_out_of_range_page_ids_are_clamped(csa2):
     judge(pw, got, k=200, n_keep=16)
 
 
+def test_sixteen_rows_per_request_long(csa2):
+    # The 8-pair scan (16 rows share one key stream) over a request of 40,000+ entries
+    # (many chunks per wave and a ragged tail), contiguous and paged, both scan modes.
+    wl = make_workload("rows16long", 49, [64 * 640 + 21, 3000], rows_per_req=[16, 2], n_needles=12)
+    _log("16 rows per request, 40,981 entries")
+    for w in (wl, to_paged(wl)):
+        refs = oracle.decode(w)
+        for scan_mode in (0, 1):
+            got = run_decode(csa2, w, scan_mode=scan_mode)
+            bad = []
+            for r, ref in enumerate(refs):
+                rep = parity.check_row(w, r, ref, got["kept"][r, :got["n_kept"][r]], got["sel"][r, :got["n_sel"][r]],
+                                       got["out"][r], got["lse"][r])
+                if not rep["ok"]:
+                    bad.append(rep)
+            _log(f"  paged {w.page_table is not None}, scan mode {scan_mode}: {len(refs)} rows, {len(bad)} bad")
+            assert not bad, "; ".join(f"row {rp['row']}: {' | '.join(rp['msgs'])}" for rp in bad[:5])
+
+
 def test_sixteen_rows_per_request_paged_with_row_len(csa2):
     # The largest row group (16 rows share one key stream: the 8-pair scan), paged, with
     # every row seeing a different prefix, in both scan modes.
