@@ -409,7 +409,7 @@ static int attn_args(const RaggedDev& g, const uint16_t* q, const uint8_t* main_
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;
-  attn_plan(g.R, sel_ld, a.tile_keys, a.split_keys, a.splits);
+  attn_plan(g.R, sel_ld, a.tile_keys, a.split_keys, a.splits, a.head_split);
   const size_t need = attn_workspace_bytes(g.R, sel_ld);
   if (need > 0) {
     if (!ws || ws_bytes < need)

@@ -510,7 +510,18 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // of a split half-full, instead of 3 + 3 + 3 + 1 tiles; 64-row attention 33.2 -> 32.3 us).
 // A tile holding at most 32 keys runs only its first half.  Finer plans with more splits
 // measured slower (32 rows: 7 splits of 96 keys against 5 of 128, +2 us per step).
-void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits) {
+// Head-split launches (see k_attn): 1 = when four workgroups per split of the plan above
+// still fit one per CU (up to 6 rows at 640 keys); 2 = also plan whole-tile splits for
+// head-split workgroups when that fits (fewer, longer splits, down to one split per row
+// and no merge).  2 measured slower where it differs: batched 32 rows 49.6 -> 52.7 us,
+// verify 48 rows 50.4 -> 60.4 us, 64-row attention 32.4 -> 39.0 us (every head-group
+// workgroup converts the whole tile, four times the conversion work under load).
+#ifndef CSA2_ATTN_HS
+#define CSA2_ATTN_HS 1
+#endif
+
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits,
+               int32_t& head_split) {
   const int max_keys = sel_ld + CSA2_SWA_MAX;
   const int tk = kAttnTileKeys;
   const int tiles = (max_keys + tk - 1) / tk;
@@ -525,11 +536,27 @@ void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_key
   if (per < tk) per = tk;
   split_keys = (int32_t)per;
   splits = (int32_t)((max_keys + per - 1) / per);
+  head_split = 0;
+  if (CSA2_ATTN_HS >= 1 && split_keys % tk == 0 && R * splits * 4 <= CSA2_ATTN_TARGET_WGS) {
+    head_split = 1;
+  } else if (CSA2_ATTN_HS >= 2) {
+    int64_t w4 = R > 0 ? (CSA2_ATTN_TARGET_WGS / 4) / R : 1;
+    if (w4 < 1) w4 = 1;
+    if (w4 > tiles) w4 = tiles;
+    const int64_t tps4 = (tiles + w4 - 1) / w4;
+    const int64_t per4 = tps4 * tk;
+    const int64_t n4 = (max_keys + per4 - 1) / per4;
+    if (R * n4 * 4 <= CSA2_ATTN_TARGET_WGS) {
+      split_keys = (int32_t)per4;
+      splits = (int32_t)n4;
+      head_split = 1;
+    }
+  }
 }
 
 size_t attn_workspace_bytes(int64_t R, int32_t sel_ld) {
-  int32_t tk, per, splits;
-  attn_plan(R, sel_ld, tk, per, splits);
+  int32_t tk, per, splits, hs;
+  attn_plan(R, sel_ld, tk, per, splits, hs);
   if (splits <= 1) return 0;
   const size_t parts = (size_t)R * splits * CSA2_HEADS;
   return parts * CSA2_D * sizeof(float) + 2 * parts * sizeof(float) + 3 * 256;
@@ -550,15 +577,10 @@ static void launch_attn_variant(const AttnArgs& a, dim3 grid, hipStream_t st) {
   }
 }
 
-// Head-split launches while four workgroups per split still fit one per CU.
-#ifndef CSA2_ATTN_HS
-#define CSA2_ATTN_HS 1
-#endif
-
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
   const bool half = a.split_keys % kAttnTileKeys != 0;
-  const bool hs = CSA2_ATTN_HS && !half && (int64_t)a.g.R * a.splits * 4 <= CSA2_ATTN_TARGET_WGS;
+  const bool hs = a.head_split != 0 && !half;
   if (hs)
     launch_attn_variant<false, true>(a, dim3(a.splits * 4, a.g.R), st);
   else if (half)

@@ -193,9 +193,11 @@ struct AttnArgs {
   float* lpart;              // [R][splits][64]
   float* out;                // [R][64][512]
   float* lse;                // [R][64]
+  int32_t head_split;        // 1: four workgroups per split, one per head group
 };
 
-void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits);
+void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits,
+               int32_t& head_split);
 size_t attn_workspace_bytes(int64_t R, int32_t sel_ld);
 hipError_t launch_attn(AttnArgs a, hipStream_t st);
 hipError_t launch_attn_main(const AttnArgs& a, hipStream_t st);
