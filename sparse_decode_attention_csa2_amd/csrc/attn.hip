@@ -20,7 +20,8 @@
 // fp32 accumulation and an online softmax between them; probabilities enter PV as
 // bf16 hi + lo parts.  Workgroups of one row write (unnormalised O, running max,
 // running sum) partials that a second kernel merges by log-sum-exp; with a single
-// split the kernel writes the result directly.
+// split the kernel writes the result directly.  Launches with few rows spread each
+// split's four head groups over four workgroups (head-split, below).
 #include <math.h>
 
 #include "csa2_internal.h"
