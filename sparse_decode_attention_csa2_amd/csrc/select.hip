@@ -10,13 +10,16 @@
 // Selection is exact.  Items (block scores, or the entries of the kept blocks) are
 // gathered once into LDS as order-preserving 32-bit keys (0 = empty item), in chunks of
 // 64; each wave owns a contiguous range of chunks, so item order is (wave, chunk, lane).
-//  - k-th largest key: keys are normalised by the workgroup minimum and an 11-bit
-//    digit of the highest bits that vary is histogrammed (2048 LDS bins); one wave
-//    scans the bins; the members of a threshold bin with at most 64 of them are
-//    ranked by (key desc, order asc) by one wave, otherwise the next digit is
-//    examined.
-//  - output: per-chunk ballots give each item its rank among the selected items, so
-//    positions come out ascending without sorting.
+//  - k-th largest key: a first histogram (2048 LDS bins) bins the scores linearly
+//    between the smallest and largest valid score; one wave scans the bins; the
+//    members of a threshold bin with at most 64 of them are ranked by (key desc, order
+//    asc) by one wave.  A larger bin (or a range without finite bins) continues with
+//    11-bit digits of the key bits: keys normalised by the workgroup minimum, the
+//    highest bits that vary first.
+//  - output: the member collection also counts each wave's keys above the threshold
+//    bin, the ranking wave adds its members' share, and per-chunk ballots then give each
+//    item its rank among the selected items, so positions come out ascending without
+//    sorting.
 // These kernels run once per row and are latency-bound: loops stay rolled (small
 // unroll factors, as instruction fetch of a large straight-line kernel would dominate),
 // and every load in a loop is unconditional (key buffers are zero-padded to whole
