@@ -289,6 +289,27 @@ def test_sparse_attn_matches_oracle(csa2, k, swa):
         assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS, f"row {r}: rel {rel:.3g} lse {dl:.3g}"
 
 
+@pytest.mark.parametrize("k,swa", [(2048, 128), (2048, 0), (700, 5)])
+def test_sparse_attn_one_row_head_split(csa2, k, swa):
+    # One row: the launch is head-split (four workgroups per split), here with up to 34
+    # splits, so the merge combines many split partials per head group.
+    _log(f"attention, one row (head-split): k {k}, window {swa}")
+    wl = make_workload("attn1", 55 + k + swa, [9000], rows_per_req=1, n_needles=4, swa_len=[swa])
+    dw = upload(wl)
+    rng = np.random.default_rng(k + swa)
+    n = wl.n_entries(0)
+    m = min(k, n)
+    sel = np.full((1, k), -1, dtype=np.int32)
+    sel[0, :m] = np.sort(rng.choice(n, size=m, replace=False))
+    n_sel = np.array([m], dtype=np.int32)
+    out, lse = csa2.sparse_attn(dw.rg, dw.q, dw.main_kv, torch.from_numpy(sel).cuda(),
+                                torch.from_numpy(n_sel).cuda(), dw.swa, dw.swa_scale, wl.sm_scale)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    ro, rl = oracle.joint_attention(oracle.bf16_value(wl.q[0]), oracle.row_keys(wl, 0, sel[0, :m]), wl.sm_scale)
+    rel, dl = parity.attn_error(out[0], lse[0], ro, rl)
+    assert rel <= parity.ATTN_REL and dl <= parity.LSE_ABS, f"rel {rel:.3g} lse {dl:.3g}"
+
+
 def test_sparse_attn_many_rows_single_split(csa2):
     # With enough rows each row's keys go to one workgroup, which normalises and writes
     # the output itself (no split partials, no merge); some rows also span several tiles.
