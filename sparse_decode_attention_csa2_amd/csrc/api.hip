@@ -655,8 +655,8 @@ int csa2_cache_write(const csa2_ragged* rg, const int64_t* row_pos, const uint16
   CHECK(check_ptr(main_kv, 16, "main_kv"));
   CHECK(check_ptr(idx_k, 4, "idx_k"));
   CHECK(check_ptr(blk_sum, 4, "blk_sum"));
-  LAUNCH(launch_cache_write(g, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, eps, main_kv, idx_k,
-                            blk_sum, reinterpret_cast<hipStream_t>(stream)),
+  LAUNCH(launch_cache_write(g, rg->max_rows_per_request, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv,
+                            gamma_idx, eps, main_kv, idx_k, blk_sum, reinterpret_cast<hipStream_t>(stream)),
          "cache write");
   return CSA2_OK;
 }

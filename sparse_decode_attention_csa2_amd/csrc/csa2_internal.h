@@ -207,10 +207,10 @@ hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
 hipError_t launch_sel_rows(const RaggedDev& g, const int32_t* sel, const int32_t* n_sel, int32_t sel_ld,
                            int32_t* rows, hipStream_t st);
 
-hipError_t launch_cache_write(const RaggedDev& g, const int64_t* row_pos, const uint16_t* kv_tok,
-                              const uint16_t* idx_tok, uint16_t* ring_kv, uint16_t* ring_idx, const float* gamma_kv,
-                              const float* gamma_idx, float eps, uint8_t* main_kv, uint8_t* idx_k, uint16_t* blk_sum,
-                              hipStream_t st);
+hipError_t launch_cache_write(const RaggedDev& g, int32_t max_rows_per_request, const int64_t* row_pos,
+                              const uint16_t* kv_tok, const uint16_t* idx_tok, uint16_t* ring_kv, uint16_t* ring_idx,
+                              const float* gamma_kv, const float* gamma_idx, float eps, uint8_t* main_kv,
+                              uint8_t* idx_k, uint16_t* blk_sum, hipStream_t st);
 hipError_t launch_debug_mxfp8(const float* x, int64_t n, float* out, hipStream_t st);
 hipError_t launch_clock_trace(uint64_t* out, int n, int interval, hipStream_t st);
 hipError_t launch_debug_dequant(int kind, const uint8_t* rec, const float* scales, int64_t n, float* out,

@@ -7,10 +7,12 @@
 // contiguous: a row pools with the previous row, only a request's first row reads the
 // ring buffer; the same fused write serves main KV and index K).
 //
-// One wave per row builds both records of the entry the row completes (lane l holds
-// main dims 8l..8l+7 and index dims 2l, 2l+1, so a 16-dim main block spans two lanes
-// and a 32-dim index block sixteen); a second launch recomputes the summaries of the
-// blocks that received entries and moves the ring slots, after every row has read them.
+// One workgroup per request, one launch: a wave per row builds both records of the
+// entry the row completes (lane l holds main dims 8l..8l+7 and index dims 2l, 2l+1, so
+// a 16-dim main block spans two lanes and a 32-dim index block sixteen); after a
+// workgroup barrier (the new records are then visible to the whole workgroup) two
+// waves recompute the summaries of the blocks that received entries, and one moves the
+// ring slot, which every row that reads it has read before the barrier.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -33,12 +35,18 @@ __device__ __forceinline__ int fp4_scale_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Value of an E2M1 code: exponent bits e = (c >> 1) & 3, mantissa bit c & 1;
-// e = 0 is subnormal (0 or 0.5), otherwise 2^(e-1) * (1 + mantissa / 2).
-__device__ __forceinline__ double e2m1_value(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const double v = e == 0u ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
-  return (c & 8u) ? -v : v;
+// Twice the value of an E2M1 code, as a signed integer: the magnitudes 0, .5, 1, 1.5,
+// 2, 3, 4, 6 of codes 0..7 doubled are 0, 1, 2, 3, 4, 6, 8, 12 (one nibble each of a
+// packed constant); bit 3 is the sign.
+__device__ __forceinline__ int e2m1_twice(uint32_t c) {
+  const int k = (int)((0xC8643210u >> (4u * (c & 7u))) & 15u);
+  return (c & 8u) ? -k : k;
+}
+
+// 2^(e - 128) for an E8M0 byte e (0..255) as a double, from its exponent field; with
+// the doubled E2M1 value above, k * 2^(e - 128) is an element's exact value.
+__device__ __forceinline__ double e8m0_half_scale(uint32_t e) {
+  return __longlong_as_double((long long)(e + 895u) << 52);
 }
 
 __device__ __forceinline__ float wave_sum_f(float v) {
@@ -93,11 +101,8 @@ __device__ __forceinline__ int64_t row_entry(const WriteArgs& a, int r, int b, i
   return t < n ? t : -1;
 }
 
-__global__ __launch_bounds__(256) void k_write_entries(WriteArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
-  if (r >= a.g.R) return;
+// Records of the entry row r completes (one wave, lane = its lane).
+__device__ void write_entry(const WriteArgs& a, int r, int lane) {
   const int b = row_request(a.g, r);
   int64_t e0, n;
   req_entries(a.g, b, e0, n);
@@ -161,11 +166,10 @@ __global__ __launch_bounds__(256) void k_write_entries(WriteArgs a) {
   }
 }
 
-// Summaries of the (at most two) blocks request b's rows wrote into, then its ring slot.
-// Lane l sums index dims 2l, 2l+1 over the block's entries.
-__global__ __launch_bounds__(64) void k_write_summaries(WriteArgs a) {
-  const int b = blockIdx.x, which = blockIdx.y;
-  const int lane = threadIdx.x;
+// Summary of block `which` (0 or 1) of the (at most two) blocks request b's rows wrote
+// into, then (which 0) its ring slot; one wave.  Lane l sums index dims 2l, 2l+1 over
+// the block's entries.
+__device__ void write_summary(const WriteArgs& a, int b, int which, int lane) {
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
   if (r1 <= r0) return;
@@ -203,12 +207,11 @@ __global__ __launch_bounds__(64) void k_write_summaries(WriteArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-          if (eb + u < cnt) {
-            // E2M1 value of each nibble times the E8M0 scale (exact in double).
-            const double sc = ldexp(1.0, (int)sb[u] - 127);
-            s0 += e2m1_value(c[u] & 15u) * sc;
-            s1 += e2m1_value(c[u] >> 4) * sc;
-          }
+          // Each element's exact value (a small integer times a power of two), summed in
+          // entry order; entries past the block's count add zero (no branch).
+          const double sc = eb + u < cnt ? e8m0_half_scale(sb[u]) : 0.0;
+          s0 += (double)e2m1_twice(c[u] & 15u) * sc;
+          s1 += (double)e2m1_twice(c[u] >> 4) * sc;
         }
       }
       const uint32_t w = bf16_rne_from_double(s0 / cnt) | (bf16_rne_from_double(s1 / cnt) << 16);
@@ -228,18 +231,32 @@ __global__ __launch_bounds__(64) void k_write_summaries(WriteArgs a) {
   }
 }
 
+// Workgroup b: the request's rows (wave w takes rows r0 + w, r0 + w + waves, ...), then
+// its block summaries and ring slot.
+__global__ __launch_bounds__(64 * CSA2_ROWS_PER_REQ_MAX) void k_write(WriteArgs a) {
+  const int b = blockIdx.x;
+  const int nw = (int)(blockDim.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int r0, r1;
+  req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
+  for (int r = r0 + wave; r < r1; r += nw) write_entry(a, r, lane);
+  __syncthreads();
+  if (wave < 2) write_summary(a, b, wave, lane);
+}
+
 }  // namespace
 
-hipError_t launch_cache_write(const RaggedDev& g, const int64_t* row_pos, const uint16_t* kv_tok,
-                              const uint16_t* idx_tok, uint16_t* ring_kv, uint16_t* ring_idx, const float* gamma_kv,
-                              const float* gamma_idx, float eps, uint8_t* main_kv, uint8_t* idx_k, uint16_t* blk_sum,
-                              hipStream_t st) {
+hipError_t launch_cache_write(const RaggedDev& g, int32_t max_rows_per_request, const int64_t* row_pos,
+                              const uint16_t* kv_tok, const uint16_t* idx_tok, uint16_t* ring_kv, uint16_t* ring_idx,
+                              const float* gamma_kv, const float* gamma_idx, float eps, uint8_t* main_kv,
+                              uint8_t* idx_k, uint16_t* blk_sum, hipStream_t st) {
   if (g.R == 0 || g.B == 0) return hipSuccess;
   WriteArgs a{g, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, eps, main_kv, idx_k, blk_sum};
-  k_write_entries<<<dim3((g.R + 3) / 4), dim3(256), 0, st>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_write_summaries<<<dim3(g.B, 2), dim3(64), 0, st>>>(a);
+  // A wave per row of the largest request (at least two, for the two summaries).
+  const int nw = max_rows_per_request < 2 ? 2 : (max_rows_per_request > CSA2_ROWS_PER_REQ_MAX ? CSA2_ROWS_PER_REQ_MAX
+                                                                                               : max_rows_per_request);
+  k_write<<<dim3(g.B), dim3(64 * nw), 0, st>>>(a);
   return hipGetLastError();
 }
 
