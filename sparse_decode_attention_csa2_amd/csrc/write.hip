@@ -49,6 +49,8 @@ __device__ __forceinline__ double e8m0_half_scale(uint32_t e) {
   return __longlong_as_double((long long)(e + 895u) << 52);
 }
 
+typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+
 __device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
@@ -93,34 +95,38 @@ struct WriteArgs {
   uint16_t* blk_sum;
 };
 
-// Entry completed by row r (-1 if none): t = (P-1)/2 for an odd position P with t < N_b.
-__device__ __forceinline__ int64_t row_entry(const WriteArgs& a, int r, int b, int64_t n) {
-  const int64_t p = a.row_pos[r];
-  if (p < 0 || (p & 1) == 0) return -1;
-  const int64_t t = (p - 1) / 2;
-  return t < n ? t : -1;
-}
-
-// Records of the entry row r completes (one wave, lane = its lane).
+// Records of the entry row r completes (one wave, lane = its lane).  Every input is
+// loaded before any record is written (the stores could otherwise hold back the index
+// vector's loads).
 __device__ void write_entry(const WriteArgs& a, int r, int lane) {
   const int b = row_request(a.g, r);
   int64_t e0, n;
   req_entries(a.g, b, e0, n);
-  const int64_t t = row_entry(a, r, b, n);
-  if (t < 0) return;
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
   const int64_t p = a.row_pos[r];
-  const bool prev_row = r - 1 >= r0 && a.row_pos[r - 1] == p - 1;
+  const int64_t pprev = a.row_pos[r > 0 ? r - 1 : 0];
+  const bool prev_row = r - 1 >= r0 && pprev == p - 1;
   const uint16_t* pk = prev_row ? a.kv_tok + (int64_t)(r - 1) * CSA2_D : a.ring_kv + (int64_t)b * CSA2_D;
   const uint16_t* pi = prev_row ? a.idx_tok + (int64_t)(r - 1) * CSA2_IDX_D : a.ring_idx + (int64_t)b * CSA2_IDX_D;
   const uint16_t* xk = a.kv_tok + (int64_t)r * CSA2_D;
   const uint16_t* xi = a.idx_tok + (int64_t)r * CSA2_IDX_D;
+  const u32x4_t va = load16(pk + 8 * lane), vb = load16(xk + 8 * lane);
+  const uint32_t wa = *reinterpret_cast<const uint32_t*>(pi + 2 * lane);
+  const uint32_t wb = *reinterpret_cast<const uint32_t*>(xi + 2 * lane);
+  const f32x4a4_t gk0 = *reinterpret_cast<const f32x4a4_t*>(a.gamma_kv + 8 * lane);
+  const f32x4a4_t gk1 = *reinterpret_cast<const f32x4a4_t*>(a.gamma_kv + 8 * lane + 4);
+  const float gi0 = a.gamma_idx[2 * lane], gi1 = a.gamma_idx[2 * lane + 1];
+  asm volatile("" ::: "memory");   // keep the loads here, ahead of the checks below
+  // Entry completed by the row: t = (P-1)/2 for an odd position P with t < N_b.
+  if (p < 0 || (p & 1) == 0) return;
+  const int64_t t = (p - 1) / 2;
+  if (t >= n) return;
   const int64_t row = entry_row(a.g, b, e0, t);
 
   // Main vector: dims 8 lane .. 8 lane + 7.
   {
-    const u32x4_t va = load16(pk + 8 * lane), vb = load16(xk + 8 * lane);
+    const float gk[8] = {gk0[0], gk0[1], gk0[2], gk0[3], gk1[0], gk1[1], gk1[2], gk1[3]};
     float y[8];
     float ss = 0.f;
 #pragma unroll
@@ -134,7 +140,7 @@ __device__ void write_entry(const WriteArgs& a, int r, int lane) {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      y[i] = y[i] * rs * a.gamma_kv[8 * lane + i];
+      y[i] = y[i] * rs * gk[i];
       amax = fmaxf(amax, fabsf(y[i]));
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));   // 16-dim block = lanes 2k, 2k+1
@@ -148,13 +154,11 @@ __device__ void write_entry(const WriteArgs& a, int r, int lane) {
   }
   // Index vector: dims 2 lane, 2 lane + 1.
   {
-    const uint32_t wa = *reinterpret_cast<const uint32_t*>(pi + 2 * lane);
-    const uint32_t wb = *reinterpret_cast<const uint32_t*>(xi + 2 * lane);
     float y0 = (bf16_lo(wa) + bf16_lo(wb)) * 0.5f, y1 = (bf16_hi(wa) + bf16_hi(wb)) * 0.5f;
     const float ss = fmaf(y1, y1, y0 * y0);
     const float rs = 1.f / sqrtf(wave_sum_f(ss) / (float)CSA2_IDX_D + a.eps);
-    y0 = y0 * rs * a.gamma_idx[2 * lane];
-    y1 = y1 * rs * a.gamma_idx[2 * lane + 1];
+    y0 = y0 * rs * gi0;
+    y1 = y1 * rs * gi1;
     float amax = fmaxf(fabsf(y0), fabsf(y1));
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));   // 32-dim block = 16 lanes
@@ -167,18 +171,33 @@ __device__ void write_entry(const WriteArgs& a, int r, int lane) {
 }
 
 // Summary of block `which` (0 or 1) of the (at most two) blocks request b's rows wrote
-// into, then (which 0) its ring slot; one wave.  Lane l sums index dims 2l, 2l+1 over
-// the block's entries.
-__device__ void write_summary(const WriteArgs& a, int b, int which, int lane) {
+// into, and (which 0) the request's ring slot; one wave.  summary_prepare, before the
+// records are written: the rows' positions, the block and the ring slot's tokens (kernel
+// inputs); summary_finish, after: the block's records summed and the stores.
+struct SummaryPrep {
+  const uint8_t* blk;   // the block's first index record
+  uint16_t* dst;        // its summary, dims 2 lane, 2 lane + 1
+  int cnt;              // entries in the block (0: no block to summarise)
+  bool ring;            // the last row waits for its partner: move its tokens to the ring
+  u32x4_t rk;
+  uint32_t ri;
+};
+
+__device__ SummaryPrep summary_prepare(const WriteArgs& a, int b, int which, int lane) {
+  SummaryPrep sp{};
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
-  if (r1 <= r0) return;
+  if (r1 <= r0) return sp;
   int64_t e0, n, bl0, nb;
   req_entries(a.g, b, e0, n);
   req_blocks(a.g, b, n, bl0, nb);
   // Lane l looks at row r0 + l (a request has at most 16 rows): one load round for all.
   static_assert(CSA2_ROWS_PER_REQ_MAX <= 64, "one row per lane");
-  const int64_t tl = r0 + lane < r1 ? row_entry(a, r0 + lane, b, n) : -1;
+  int64_t tl = -1;
+  if (r0 + lane < r1) {
+    const int64_t p = a.row_pos[r0 + lane];
+    tl = (p >= 0 && (p & 1) != 0 && (p - 1) / 2 < n) ? (p - 1) / 2 : -1;
+  }
   int64_t tmin = tl >= 0 ? tl : INT64_MAX, tmax = tl;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -186,63 +205,73 @@ __device__ void write_summary(const WriteArgs& a, int b, int which, int lane) {
     tmin = om < tmin ? om : tmin;
     tmax = ox > tmax ? ox : tmax;
   }
-  if (tmin == INT64_MAX) tmin = -1;
-  if (tmin >= 0) {
+  if (tmin != INT64_MAX) {
     const int64_t j = tmin / CSA2_BLOCK + which;
     if (j <= tmax / CSA2_BLOCK && j < nb) {
-      const int cnt = (int)min<int64_t>(CSA2_BLOCK, n - j * CSA2_BLOCK);
-      // A block's entries are consecutive pool rows (a page, with paged pools).  Their
-      // bytes are loaded kB at a time (independent loads, clamped to the block's last
-      // entry) and summed in entry order.
-      const uint8_t* blk = a.idx_k + entry_row(a.g, b, e0, j * CSA2_BLOCK) * CSA2_IDX_BYTES;
-      constexpr int kB = 64;
-      double s0 = 0.0, s1 = 0.0;
-      for (int eb = 0; eb < cnt; eb += kB) {
-        uint32_t c[kB], sb[kB];
-#pragma unroll
-        for (int u = 0; u < kB; ++u) {
-          const uint8_t* rec = blk + min(eb + u, cnt - 1) * CSA2_IDX_BYTES;
-          c[u] = rec[lane];
-          sb[u] = rec[64 + lane / 16];
-        }
-#pragma unroll
-        for (int u = 0; u < kB; ++u) {
-          // Each element's exact value (a small integer times a power of two), summed in
-          // entry order; entries past the block's count add zero (no branch).
-          const double sc = eb + u < cnt ? e8m0_half_scale(sb[u]) : 0.0;
-          s0 += (double)e2m1_twice(c[u] & 15u) * sc;
-          s1 += (double)e2m1_twice(c[u] >> 4) * sc;
-        }
-      }
-      const uint32_t w = bf16_rne_from_double(s0 / cnt) | (bf16_rne_from_double(s1 / cnt) << 16);
-      *reinterpret_cast<uint32_t*>(a.blk_sum + block_row(a.g, b, bl0, j) * CSA2_IDX_D + 2 * lane) = w;
+      // A block's entries are consecutive pool rows (a page, with paged pools).
+      sp.cnt = (int)min<int64_t>(CSA2_BLOCK, n - j * CSA2_BLOCK);
+      sp.blk = a.idx_k + entry_row(a.g, b, e0, j * CSA2_BLOCK) * CSA2_IDX_BYTES;
+      sp.dst = a.blk_sum + block_row(a.g, b, bl0, j) * CSA2_IDX_D + 2 * lane;
     }
   }
   // Ring slot: the last row's token when it waits for its partner (even position).
   if (which == 0) {
     const int64_t p = a.row_pos[r1 - 1];
     if (p >= 0 && (p & 1) == 0) {
-      const uint16_t* xk = a.kv_tok + (int64_t)(r1 - 1) * CSA2_D;
-      const uint16_t* xi = a.idx_tok + (int64_t)(r1 - 1) * CSA2_IDX_D;
-      *reinterpret_cast<u32x4_t*>(a.ring_kv + (int64_t)b * CSA2_D + 8 * lane) = load16(xk + 8 * lane);
-      *reinterpret_cast<uint32_t*>(a.ring_idx + (int64_t)b * CSA2_IDX_D + 2 * lane) =
-          *reinterpret_cast<const uint32_t*>(xi + 2 * lane);
+      sp.ring = true;
+      sp.rk = load16(a.kv_tok + (int64_t)(r1 - 1) * CSA2_D + 8 * lane);
+      sp.ri = *reinterpret_cast<const uint32_t*>(a.idx_tok + (int64_t)(r1 - 1) * CSA2_IDX_D + 2 * lane);
     }
+  }
+  return sp;
+}
+
+__device__ void summary_finish(const WriteArgs& a, int b, const SummaryPrep& sp, int lane) {
+  if (sp.cnt > 0) {
+    // The block's bytes are loaded kB at a time (independent loads, clamped to the
+    // block's last entry) and each element's exact value (a small integer times a power
+    // of two) is summed in entry order; entries past the block's count add zero.
+    constexpr int kB = 64;
+    double s0 = 0.0, s1 = 0.0;
+    for (int eb = 0; eb < sp.cnt; eb += kB) {
+      uint32_t c[kB], sb[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const uint8_t* rec = sp.blk + min(eb + u, sp.cnt - 1) * CSA2_IDX_BYTES;
+        c[u] = rec[lane];
+        sb[u] = rec[64 + lane / 16];
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const double sc = eb + u < sp.cnt ? e8m0_half_scale(sb[u]) : 0.0;
+        s0 += (double)e2m1_twice(c[u] & 15u) * sc;
+        s1 += (double)e2m1_twice(c[u] >> 4) * sc;
+      }
+    }
+    const uint32_t w = bf16_rne_from_double(s0 / sp.cnt) | (bf16_rne_from_double(s1 / sp.cnt) << 16);
+    *reinterpret_cast<uint32_t*>(sp.dst) = w;
+  }
+  if (sp.ring) {
+    *reinterpret_cast<u32x4_t*>(a.ring_kv + (int64_t)b * CSA2_D + 8 * lane) = sp.rk;
+    *reinterpret_cast<uint32_t*>(a.ring_idx + (int64_t)b * CSA2_IDX_D + 2 * lane) = sp.ri;
   }
 }
 
 // Workgroup b: the request's rows (wave w takes rows r0 + w, r0 + w + waves, ...), then
-// its block summaries and ring slot.
+// its block summaries and ring slot (whose preparation, which reads only kernel inputs,
+// runs before the rows).
 __global__ __launch_bounds__(64 * CSA2_ROWS_PER_REQ_MAX) void k_write(WriteArgs a) {
   const int b = blockIdx.x;
   const int nw = (int)(blockDim.x >> 6);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  SummaryPrep sp{};
+  if (wave < 2) sp = summary_prepare(a, b, wave, lane);
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
   for (int r = r0 + wave; r < r1; r += nw) write_entry(a, r, lane);
   __syncthreads();
-  if (wave < 2) write_summary(a, b, wave, lane);
+  if (wave < 2) summary_finish(a, b, sp, lane);
 }
 
 }  // namespace
