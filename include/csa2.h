@@ -295,7 +295,10 @@ int csa2_debug_dequant(int32_t kind, const uint8_t* records, const float* scales
                        void* stream);
 
 /* Test hook: the attention kernel's MXFP8 rounding (CSA2_QP_MXFP8) over x[0 .. n-1] in
- * blocks of 32 consecutive values (n a multiple of 32), results as exact fp32 in out. */
+ * blocks of 32 consecutive values (n a multiple of 32), results as exact fp32 in out.
+ * A block whose 32 values are all bf16 values goes through the bf16-input rounding the
+ * kernel applies to the query; any other block through the fp32-input rounding it
+ * applies to the probabilities. */
 int csa2_debug_mxfp8(const float* x, int64_t n, float* out, void* stream);
 
 /* Measurement hook, for callers that want the bandwidth a plain streaming read reaches

@@ -236,7 +236,9 @@ hipError_t launch_clock_trace(uint64_t* out, int n, int interval, hipStream_t st
 }
 
 // Test hook: lane (i, g) of a wave rounds values 8g .. 8g+7 of block 16w + i (w = the
-// wave's index in the grid) with the attention kernel's block helper.
+// wave's index in the grid) with the attention kernel's block helpers: blocks whose 32
+// values are all bf16 values take the bf16-input rounding (the query's), the others the
+// fp32-input one (the probabilities').
 __global__ __launch_bounds__(256) void k_debug_mxfp8(const float* x, int64_t nblocks, float* out) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + (lane & 15);
@@ -244,8 +246,20 @@ __global__ __launch_bounds__(256) void k_debug_mxfp8(const float* x, int64_t nbl
   const bool ok = blk < nblocks;
   float v[8];
   for (int j = 0; j < 8; ++j) v[j] = ok ? x[blk * 32 + 8 * g + j] : 0.f;
-  float r[8];
+  uint32_t exact = 1u;
+  u32x4_t w;
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = __float_as_uint(v[2 * q]), b = __float_as_uint(v[2 * q + 1]);
+    exact &= ((a | b) & 0xFFFFu) == 0u ? 1u : 0u;
+    w[q] = (a >> 16) | (b & 0xFFFF0000u);
+  }
+  exact &= __shfl_xor(exact, 16, 64);
+  exact &= __shfl_xor(exact, 32, 64);
+  float r[8], rb[8];
   bf16x8_words_to_f32(mx8_round_block_bf16x8(v), r);
+  bf16x8_words_to_f32(mx8_round_block_bf16(as_bf16x8(w)), rb);
+  if (exact)
+    for (int j = 0; j < 8; ++j) r[j] = rb[j];
   if (ok)
     for (int j = 0; j < 8; ++j) out[blk * 32 + 8 * g + j] = r[j];
 }

@@ -241,11 +241,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     // MXFP8 route: block st of 32 dims = this lane's 8 values and those of lanes xor 16
     // and xor 32 (rounded while the first tile's records are in flight).
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      float v[8];
-      bf16x8_words_to_f32(qb[st], v);
-      qb[st] = mx8_round_block_bf16x8(v);
-    }
+    for (int st = 0; st < 8; ++st) qb[st] = mx8_round_block_bf16(qb[st]);
   }
 
   // Transposed-read offsets (elements): lane (g, i = 4k + q) points at key 4g + k of a

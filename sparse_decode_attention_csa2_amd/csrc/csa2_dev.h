@@ -131,15 +131,15 @@ __device__ __forceinline__ bf16x8_t mx8_round8_bf16x8(const float (&v)[8], int s
   u32x4_t w;
 #if CSA2_MX_HW_CVT
   // gfx950's scaled FP8 conversions: x / 2^s to E4M3FN (round to nearest even) and back
-  // times 2^s, after clamping to the largest grid value (448 units) so nothing overflows.
+  // times 2^s straight to bf16 (exact: an E4M3 value times 2^s), after clamping to the largest grid value (448 units) so nothing overflows.
   typedef short v2s __attribute__((ext_vector_type(2)));
   const float sc = __builtin_ldexpf(1.f, s), lim = __builtin_ldexpf(448.f, s);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float a = __builtin_amdgcn_fmed3f(v[2 * q], -lim, lim), b = __builtin_amdgcn_fmed3f(v[2 * q + 1], -lim, lim);
     const v2s p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, sc, false);
-    const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)__builtin_bit_cast(int, p), sc, false);
-    w[q] = pack_bf16x2_rne(f[0], f[1]);
+    w[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                            (uint32_t)__builtin_bit_cast(int, p), sc, false));
   }
 #else
 #pragma unroll
@@ -157,6 +157,54 @@ __device__ __forceinline__ bf16x8_t mx8_round_block_bf16x8(const float (&v)[8]) 
   for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
   amax = xor32_max(xor16_max(amax));
   return mx8_round8_bf16x8(v, mx8_scale_exp(amax));
+}
+
+// Packed 16-bit unsigned max / min of two words (v_pk_max_u16, v_pk_min_u16).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
+
+// The same MXFP8 rounding for a block of bf16 values (the query), without leaving bf16:
+// a bf16 magnitude's bits order like its value, so the block maximum is a packed 16-bit
+// integer max (then over lanes xor 16 and xor 32), its exponent field f gives the shared
+// exponent s = max(f, 8) - 135 (f - 127 = floor(log2 amax) for normal amax; zero and
+// subnormal maxima give f = 0 and s = -127), the saturation at 448 * 2^s is a packed
+// integer min of the magnitudes against that value's bits (exponent field s + 135,
+// mantissa 0x60), and gfx950's scaled conversions take bf16 pairs to E4M3FN (round to
+// nearest even) and back.
+__device__ __forceinline__ bf16x8_t mx8_round_block_bf16(bf16x8_t x) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, x);
+  u32x4_t mag;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mag[q] = w[q] & 0x7FFF7FFFu;
+  uint32_t mm = pk_max_u16(pk_max_u16(mag[0], mag[1]), pk_max_u16(mag[2], mag[3]));
+  const auto p16 = __builtin_amdgcn_permlane16_swap(mm, mm, false, false);
+  mm = pk_max_u16(p16[0], p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(mm, mm, false, false);
+  mm = pk_max_u16(p32[0], p32[1]);
+  const uint32_t f = max(max(mm & 0xFFFFu, mm >> 16) >> 7, 8u);   // s + 135
+  const float sc = e8m0_operand(f - 8u);                           // 2^s
+  const uint32_t lim = (f << 7) | 0x60u;                           // bf16 bits of 448 * 2^s
+  const uint32_t lim2 = lim | (lim << 16);
+  u32x4_t out;
+#pragma unroll
+  for (int q = 0; q < 4; q += 2) {
+    const uint32_t c0 = (w[q] & 0x80008000u) | pk_min_u16(mag[q], lim2);
+    const uint32_t c1 = (w[q + 1] & 0x80008000u) | pk_min_u16(mag[q + 1], lim2);
+    v2s e = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s{0, 0}, __builtin_bit_cast(bf16x2_t, c0), sc, false);
+    e = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(e, __builtin_bit_cast(bf16x2_t, c1), sc, true);
+    const uint32_t codes = __builtin_bit_cast(uint32_t, e);
+    out[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, sc, false));
+    out[q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, sc, true));
+  }
+  return __builtin_bit_cast(bf16x8_t, out);
 }
 
 // Widen 8 bf16 to fp32 through the packed 32-bit words (integer shifts only).

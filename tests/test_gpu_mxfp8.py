@@ -78,6 +78,15 @@ def test_mxfp8_rounding_matches_oracle(csa2):
     z[[1, 5]] = [0.0, z.max() * 1e-5]
     blocks += [z, np.zeros(32)]
     x = np.stack(blocks).astype(np.float32)
+    # The same blocks rounded to bf16 (the query's type) take the bf16-input rounding:
+    # every grid point and midpoint above is a bf16 value already; add the random blocks
+    # as bf16 and a block of bf16 subnormals (shared exponent at its floor of -127; the
+    # results are multiples of 2^-133, so bf16 holds them).
+    xb = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    sub = (rng.integers(1, 128, 32) * rng.choice([-1.0, 1.0], 32) * 2.0 ** -133).astype(np.float32)
+    x = np.concatenate([x, xb, sub[None]])
+    exact = (x.view(np.uint32) & 0xFFFF) == 0
+    assert exact[-1].all() and exact.all(axis=1).sum() >= x.shape[0] // 2
     got = csa2.debug_mxfp8(torch.from_numpy(x.reshape(-1)).cuda()).cpu().numpy().reshape(x.shape)
     ref = oracle.mxfp8_round(x.astype(np.float64))
     _log(f"mxfp8 rounding: {x.shape[0]} blocks")
