@@ -34,6 +34,14 @@ namespace {
 #endif
 constexpr int KLS = CSA2_ATTN_KLS;   // Kl row stride in bf16 (512 + 16: rows 32 B apart modulo 256 B)
 static_assert(KLS >= 512 && KLS % 8 == 0, "Kl rows hold 512 bf16, 16-byte aligned");
+
+// Column of dim d (a multiple of 4) in row `row` of Kl: each 32-dim (64-B) chunk holds
+// its four 16-B pieces in the order piece ^ ((row >> 2) & 3).  The dequantising threads
+// write 16-B pieces of rows 2 apart at the same chunk, which without the swizzle fall
+// into the same banks (measured 23.6 conflict cycles per 16-B store); with it every
+// 16-B store, the QK^T reads (rows 16b + lane % 16) and the transposing PV reads (rows
+// 4g + ...) are conflict-free.
+__device__ __forceinline__ int kl_col(int row, int d) { return d ^ (((row >> 2) & 3) << 3); }
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplitKeys = CSA2_K_MAX + CSA2_SWA_MAX;   // positions of one split staged in LDS
 constexpr int kAttnTileKeys = 64;
@@ -244,19 +252,26 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     for (int st = 0; st < 8; ++st) qb[st] = mx8_round_block_bf16(qb[st]);
   }
 
-  // Transposed-read offsets (elements): lane (g, i = 4k + q) points at key 4g + k of a
-  // 16-key half and dims 4q .. 4q+3 of a 16-dim tile.
-  const int tr_off = (4 * g + (ln >> 2)) * KLS + (HS ? 64 * wave : 256 * dh) + 4 * (ln & 3);
+  // Kl offsets with the swizzle (kl_col) folded in.  QK^T: lane (g, ln) reads dims 8g..
+  // of a 32-dim chunk of row 16b + ln, whose swizzle term is (ln >> 2) & 3 for every b.
+  const int qk_g = kl_col(ln, 8 * g);
+  // Transposed reads: lane (g, i = 4k + q) points at key 4g + k of a 16-key half and dims
+  // 4q .. 4q+3 of a 16-dim tile; those rows' swizzle term is g, which moves the lane's
+  // 8 bytes within the tile's 64-B chunk differently for even and odd 16-dim tiles.
+  const int tr_row = (4 * g + (ln >> 2)) * KLS + (HS ? 64 * wave : 256 * dh);
+  const int tr_off[2] = {tr_row + kl_col(4 * g, 4 * (ln & 3)), tr_row + kl_col(4 * g, 16 + 4 * (ln & 3)) - 16};
 
   for (int kt = k_begin; kt < k_end; kt += TK) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       uint32_t w[16];
       convert_key(kr[e], ch, w);
-      uint16_t* k0 = Kl + (32 * u + 2 * kp + e) * KLS + 32 * ch;
+      const int row = 32 * u + 2 * kp + e;
+      uint16_t* k0 = Kl + row * KLS;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<u32x4_t*>(k0 + 8 * q) = u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+        *reinterpret_cast<u32x4_t*>(k0 + kl_col(row, 32 * ch + 8 * q)) =
+            u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
       if (ch == 0) {
         const int key = 32 * u + 2 * kp + e;
         ksc[key] = kr[e].kind == 2 ? __uint_as_float(kr[e].sc) : (kr[e].kind == 1 ? 1.f : 0.f);
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const bf16x8_t ak =
-            as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * kb + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * kb + ln) * KLS + 256 * dh + 32 * st + qk_g));
         sk = mfma16x16x32(ak, qb[st], sk);
       }
 #pragma unroll
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int b = 0; b < NB / 2; ++b) {
           const bf16x8_t ak =
-              as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+              as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + qk_g));
           s[b] = mfma16x16x32(ak, qb[st], s[b]);
         }
       }
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const bf16x8_t ak =
-              as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + 8 * g));
+              as_bf16x8(*reinterpret_cast<const u32x4_t*>(Kl + (16 * b + ln) * KLS + 256 * dh + 32 * st + qk_g));
           s[b] = mfma16x16x32(ak, qb[st], s[b]);
         }
       }
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
         bf16x8_t av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const uint16_t* p = Kl + tr_off + 32 * c * KLS + 16 * (t0 + v);
+          const uint16_t* p = Kl + tr_off[(t0 + v) & 1] + 32 * c * KLS + 16 * (t0 + v);
           const u32x2_t lo = lds_read_tr16(p);
           const u32x2_t hi = lds_read_tr16(p + 16 * KLS);
           av[v] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
