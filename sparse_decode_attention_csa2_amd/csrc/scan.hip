@@ -38,10 +38,10 @@ typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
 #define CSA2_SCAN_WG_STAGE 1
 #endif
 constexpr int kMaxIters = CSA2_SCAN_MAX_ITERS;      // chunks per wave, at most
-// Entry-only scans on the contiguous-read path: up to 14 chunks per wave, so that the
-// stage (14 KiB) and the key slots (17 KiB) leave room for kLdskWgsPerCu workgroups per
-// CU in 160 KiB of LDS.
-constexpr int kMaxItersLdsk = 14;
+// Entry-only scans on the contiguous-read path: up to 13 chunks per wave, so that the
+// score stage (13 KiB) and the key slots (18 KiB) leave room for kLdskWgsPerCu
+// workgroups per CU in 160 KiB of LDS.
+constexpr int kMaxItersLdsk = 13;
 constexpr int kLdskWgsPerCu = 5;
 #ifndef CSA2_SCAN_ONE_ROUND
 #define CSA2_SCAN_ONE_ROUND 1
@@ -251,9 +251,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       }
     };
     // Contiguous reads: each wave's loaded chunk is stored to its LDS slot of 64 x 68
-    // bytes and read back in the MFMA lane layout.
-    constexpr int kStageWords = 64 * CSA2_IDX_BYTES / 4;
+    // bytes and read back in the MFMA lane layout.  Every 4 entries (17 16-byte pieces)
+    // the slot skips one piece: the read-back's dword pairs (entries 68 bytes apart)
+    // otherwise meet in the same banks two by two (32 conflict cycles per chunk in a
+    // probe of the pattern; none with the skip, which leaves 14 in the stores).
+    constexpr int kStageWords = 64 * CSA2_IDX_BYTES / 4 + 4 * 15;
     __shared__ __align__(16) uint32_t kstage[kLdsKeys ? kWaves : 1][kLdsKeys ? kStageWords : 4];
+    // First word of 16-byte piece pc (< 272) of a chunk in its slot: pc + pc / 17 pieces
+    // (pc * 241 >> 12 == pc / 17 for pc < 4,096).
+    auto stage_word = [](int pc) { return 4 * (pc + ((pc * 241) >> 12)); };
     bf16x8_t qa[MAXPAIRS][4];
     float wv[MAXPAIRS][4];
     const int nrows = r1 - r0;
@@ -340,7 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       float sc[kGroups];
 #pragma unroll
       for (int gi = 0; gi < kGroups; ++gi) {
-        const uint32_t* w = kst + (16 * gi + m) * (CSA2_IDX_BYTES / 4);
+        const int e = 16 * gi + m;   // entry of the chunk; 17 words each, a piece skipped per 4
+        const uint32_t* w = kst + e * (CSA2_IDX_BYTES / 4) + 4 * (e >> 2);
         kcv[gi] = u32x4_t{w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]};
         sc[gi] = __uint_as_float(__builtin_amdgcn_alignbit(w[16], w[16], srot) & 0x7F800000u);
       }
@@ -353,8 +360,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       if constexpr (kLdsKeys) {
         uint32_t* kst = kstage[wave];
 #pragma unroll
-        for (int q = 0; q < kGroups; ++q) *reinterpret_cast<u32x4_t*>(kst + 4 * lane + 256 * q) = ck.kc[q];
-        if (lane < 16) *reinterpret_cast<u32x4_t*>(kst + 1024 + 4 * lane) = ck.kc[kGroups];
+        for (int q = 0; q < kGroups; ++q) *reinterpret_cast<u32x4_t*>(kst + stage_word(lane + 64 * q)) = ck.kc[q];
+        if (lane < 16) *reinterpret_cast<u32x4_t*>(kst + stage_word(256 + lane)) = ck.kc[kGroups];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
