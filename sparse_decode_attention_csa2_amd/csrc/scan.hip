@@ -437,6 +437,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         // One chunk in registers: once it is staged to LDS the next chunk's loads go out
         // before this chunk is scored (64 x 65,536-entry scan 53.1-55.2 -> 51.8-53.6 us
         // over runs of 200 launches; scoring first and then loading was the slower order).
+        // The compiler would sink the loads below the scoring (their registers are free
+        // for the conversions there); a memory clobber keeps them ahead of it, at 96
+        // VGPRs (still five waves per SIMD): 52.2 -> 51.8 us, 1M-context batch 52.0 ->
+        // 51.1 us (medians of eight alternating runs of 200 launches).
         start(std::true_type{});
         for (int c = 0; c < iters; ++c) {
           const int lb = lb0 + c * kStep;
@@ -444,6 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
           wait_vmcnt<0>();
           stage(ring[0]);
           issue(ring[0], lb + kStep);
+          asm volatile("" ::: "memory");
           score_slot(kstage[wave], lb);
         }
       } else {
