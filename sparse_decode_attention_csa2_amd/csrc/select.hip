@@ -30,7 +30,13 @@
 namespace csa2 {
 namespace {
 
-constexpr int NT = 512;
+// Threads per row's workgroup: 1,024 (16 waves) walks each pass over a one-row fine
+// stage's 4,160 candidates in half the chunks per wave of 512 (one-row step 29.0 ->
+// 28.5 us, 1M-context step 85.3 -> 83.7 us, identical results).
+#ifndef CSA2_SEL_THREADS
+#define CSA2_SEL_THREADS 1024
+#endif
+constexpr int NT = CSA2_SEL_THREADS;
 constexpr int NW = NT / kWave;
 #ifndef CSA2_SEL_DIGIT
 #define CSA2_SEL_DIGIT 11
@@ -49,13 +55,17 @@ constexpr int kMemMax = CSA2_SEL_MEMMAX;                     // bin members reso
 static_assert(kMemMax >= 1 && kMemMax <= 64, "members are ranked one per lane");
 constexpr int kMaxCand = (CSA2_KEEP_MAX + 1) * CSA2_BLOCK;   // 8256 candidate slots
 constexpr int kLdsBlocks = 16384;                            // block keys held in LDS
-// Gather batch per thread: 9 covers a fine stage of up to 72 kept blocks (4,608
-// candidates) in one round of loads.  Every load of a batch is issued (clamped), so a
-// larger batch only adds loads: 16 made the one-row step 1.5 us slower.
+// Gather batch per thread: enough for a fine stage of up to 72 kept blocks (4,608
+// candidates) in one round of loads (5 at 1,024 threads).  Every load of a batch is issued
+// (clamped), so a larger batch only adds loads: 16 made the one-row step 1.5 us slower.
 #ifndef CSA2_SEL_GATHER_BATCH
-#define CSA2_SEL_GATHER_BATCH 9
+#define CSA2_SEL_GATHER_BATCH ((4608 + NT - 1) / NT)
 #endif
 constexpr int kGB = CSA2_SEL_GATHER_BATCH;                   // gather batch per thread
+// Rows of at most this many block slots rank their blocks after one round of loads
+// (kSmallRowBlocks / NT per thread, issued before the row's offsets are known).
+constexpr int kSmallRowBlocks = 1024;
+static_assert(kSmallRowBlocks % NT == 0, "whole loads per thread");
 static_assert(kMaxCand >= CSA2_TOPK_ALL_MAX, "candidate buffer");
 static_assert(kLdsBlocks >= kMaxCand, "shared key buffer");
 static_assert(kLdsBlocks >= kSelSliceCand && kSelSlice % kWave == 0, "sliced coarse stage buffers");
@@ -653,13 +663,13 @@ __global__ __launch_bounds__(NT) void k_block_slices(SelectArgs a) {
 // Both stages for one row; the block keys and the candidate keys share one LDS buffer.
 // CMODE 0: all blocks ranked from LDS (first batch prefetched); 1: rows may have more
 // blocks than LDS holds; 2: the sliced coarse stage's candidates; 3: as 0 for rows of at
-// most 2 x NT block slots, whose whole gather is two loads per thread (a batch sized for
-// more blocks would issue loads that only repeat the last slot).
+// most kSmallRowBlocks block slots, whose whole gather is one round of loads (a batch
+// sized for more blocks would issue loads that only repeat the last slot).
 template <bool PAGED, int CMODE>
 __global__ __launch_bounds__(NT) void k_select_fused(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
-  constexpr int GBC = CMODE == 3 ? 2 : kGB;
+  constexpr int GBC = CMODE == 3 ? kSmallRowBlocks / NT : kGB;
   const int r = blockIdx.x;
   float pre[GBC];
   if (CMODE == 0 || CMODE == 3) prefetch_blocks(a, r, pre);
@@ -701,7 +711,7 @@ hipError_t launch_select_fused(SelectArgs a, hipStream_t st) {
 #ifndef CSA2_SEL_SMALL_ROWS
 #define CSA2_SEL_SMALL_ROWS 1
 #endif
-  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : (CSA2_SEL_SMALL_ROWS && a.blk_ld <= 2 * NT ? 3 : 0));
+  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : (CSA2_SEL_SMALL_ROWS && a.blk_ld <= kSmallRowBlocks ? 3 : 0));
   const dim3 grid(a.g.R), block(NT);
   if (a.g.page_table) {
     if (mode == 2) k_select_fused<true, 2><<<grid, block, 0, st>>>(a);
