@@ -10,8 +10,9 @@
 // One workgroup per request, one launch: a wave per row builds both records of the
 // entry the row completes (lane l holds main dims 8l..8l+7 and index dims 2l, 2l+1, so
 // a 16-dim main block spans two lanes and a 32-dim index block sixteen); after a
-// workgroup barrier (the new records are then visible to the whole workgroup) two
-// waves recompute the summaries of the blocks that received entries, and one moves the
+// workgroup barrier (the new records are then visible to the whole workgroup) four
+// waves per block sum a quarter of the records of each block that received entries,
+// the quarters meet in LDS, one wave per block stores the summary, and one moves the
 // ring slot, which every row that reads it has read before the barrier.
 #include "csa2_internal.h"
 
@@ -171,9 +172,10 @@ __device__ void write_entry(const WriteArgs& a, int r, int lane) {
 }
 
 // Summary of block `which` (0 or 1) of the (at most two) blocks request b's rows wrote
-// into, and (which 0) the request's ring slot; one wave.  summary_prepare, before the
-// records are written: the rows' positions, the block and the ring slot's tokens (kernel
-// inputs); summary_finish, after: the block's records summed and the stores.
+// into, and the request's ring slot.  summary_prepare, before the records are written:
+// the rows' positions, the block and (ring) the ring slot's tokens, all kernel inputs;
+// summary_part, after: a quarter of the block's records summed; summary_finish: the
+// quarters added and the stores.
 struct SummaryPrep {
   const uint8_t* blk;   // the block's first index record
   uint16_t* dst;        // its summary, dims 2 lane, 2 lane + 1
@@ -183,7 +185,7 @@ struct SummaryPrep {
   uint32_t ri;
 };
 
-__device__ SummaryPrep summary_prepare(const WriteArgs& a, int b, int which, int lane) {
+__device__ SummaryPrep summary_prepare(const WriteArgs& a, int b, int which, bool ring, int lane) {
   SummaryPrep sp{};
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
@@ -215,7 +217,7 @@ __device__ SummaryPrep summary_prepare(const WriteArgs& a, int b, int which, int
     }
   }
   // Ring slot: the last row's token when it waits for its partner (even position).
-  if (which == 0) {
+  if (ring) {
     const int64_t p = a.row_pos[r1 - 1];
     if (p >= 0 && (p & 1) == 0) {
       sp.ring = true;
@@ -226,27 +228,38 @@ __device__ SummaryPrep summary_prepare(const WriteArgs& a, int b, int which, int
   return sp;
 }
 
-__device__ void summary_finish(const WriteArgs& a, int b, const SummaryPrep& sp, int lane) {
+// Part q (of kSumParts) of a block's sum: entries [16q, 16q + 16), loaded at once
+// (clamped to the block's last entry); each element's exact value (a small integer times
+// a power of two) is summed in entry order, entries past the block's count adding zero.
+constexpr int kSumParts = 4;
+constexpr int kSumPart = CSA2_BLOCK / kSumParts;
+__device__ void summary_part(const SummaryPrep& sp, int q, int lane, double& s0, double& s1) {
+  s0 = 0.0;
+  s1 = 0.0;
+  if (sp.cnt <= 0) return;
+  uint32_t c[kSumPart], sb[kSumPart];
+#pragma unroll
+  for (int u = 0; u < kSumPart; ++u) {
+    const uint8_t* rec = sp.blk + min(kSumPart * q + u, sp.cnt - 1) * CSA2_IDX_BYTES;
+    c[u] = rec[lane];
+    sb[u] = rec[64 + lane / 16];
+  }
+#pragma unroll
+  for (int u = 0; u < kSumPart; ++u) {
+    const double sc = kSumPart * q + u < sp.cnt ? e8m0_half_scale(sb[u]) : 0.0;
+    s0 += (double)e2m1_twice(c[u] & 15u) * sc;
+    s1 += (double)e2m1_twice(c[u] >> 4) * sc;
+  }
+}
+
+// The block's summary from its parts' sums (added in part order) and the ring slot.
+__device__ void summary_finish(const WriteArgs& a, int b, const SummaryPrep& sp, const double (*part)[2], int lane) {
   if (sp.cnt > 0) {
-    // The block's bytes are loaded kB at a time (independent loads, clamped to the
-    // block's last entry) and each element's exact value (a small integer times a power
-    // of two) is summed in entry order; entries past the block's count add zero.
-    constexpr int kB = 64;
-    double s0 = 0.0, s1 = 0.0;
-    for (int eb = 0; eb < sp.cnt; eb += kB) {
-      uint32_t c[kB], sb[kB];
+    double s0 = part[0][0], s1 = part[0][1];
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const uint8_t* rec = sp.blk + min(eb + u, sp.cnt - 1) * CSA2_IDX_BYTES;
-        c[u] = rec[lane];
-        sb[u] = rec[64 + lane / 16];
-      }
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const double sc = eb + u < sp.cnt ? e8m0_half_scale(sb[u]) : 0.0;
-        s0 += (double)e2m1_twice(c[u] & 15u) * sc;
-        s1 += (double)e2m1_twice(c[u] >> 4) * sc;
-      }
+    for (int q = 1; q < kSumParts; ++q) {
+      s0 += part[q][0];
+      s1 += part[q][1];
     }
     const uint32_t w = bf16_rne_from_double(s0 / sp.cnt) | (bf16_rne_from_double(s1 / sp.cnt) << 16);
     *reinterpret_cast<uint32_t*>(sp.dst) = w;
@@ -257,21 +270,40 @@ __device__ void summary_finish(const WriteArgs& a, int b, const SummaryPrep& sp,
   }
 }
 
-// Workgroup b: the request's rows (wave w takes rows r0 + w, r0 + w + waves, ...), then
-// its block summaries and ring slot (whose preparation, which reads only kernel inputs,
-// runs before the rows).
+// Workgroup b (at least 2 x kSumParts waves): the request's rows (wave w takes rows
+// r0 + w, r0 + w + waves, ...), then its block summaries: wave w < 2 kSumParts sums
+// part w / 2 of block w % 2 (the preparation, which reads only kernel inputs, runs before
+// the rows), the parts meet in LDS, and waves 0 and 1 add them in part order and store
+// the summaries (and, wave 0, the ring slot).
 __global__ __launch_bounds__(64 * CSA2_ROWS_PER_REQ_MAX) void k_write(WriteArgs a) {
+  __shared__ double psum[2][kSumParts][64][2];
   const int b = blockIdx.x;
   const int nw = (int)(blockDim.x >> 6);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const bool summer = wave < 2 * kSumParts;
   SummaryPrep sp{};
-  if (wave < 2) sp = summary_prepare(a, b, wave, lane);
+  if (summer) sp = summary_prepare(a, b, wave & 1, wave == 0, lane);   // wave 0 moves the ring slot
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
   for (int r = r0 + wave; r < r1; r += nw) write_entry(a, r, lane);
   __syncthreads();
-  if (wave < 2) summary_finish(a, b, sp, lane);
+  if (summer) {
+    double s0, s1;
+    summary_part(sp, wave >> 1, lane, s0, s1);
+    psum[wave & 1][wave >> 1][lane][0] = s0;
+    psum[wave & 1][wave >> 1][lane][1] = s1;
+  }
+  __syncthreads();
+  if (wave < 2) {
+    double part[kSumParts][2];
+#pragma unroll
+    for (int q = 0; q < kSumParts; ++q) {
+      part[q][0] = psum[wave][q][lane][0];
+      part[q][1] = psum[wave][q][lane][1];
+    }
+    summary_finish(a, b, sp, part, lane);
+  }
 }
 
 }  // namespace
@@ -282,9 +314,12 @@ hipError_t launch_cache_write(const RaggedDev& g, int32_t max_rows_per_request, 
                               uint8_t* idx_k, uint16_t* blk_sum, hipStream_t st) {
   if (g.R == 0 || g.B == 0) return hipSuccess;
   WriteArgs a{g, row_pos, kv_tok, idx_tok, ring_kv, ring_idx, gamma_kv, gamma_idx, eps, main_kv, idx_k, blk_sum};
-  // A wave per row of the largest request (at least two, for the two summaries).
-  const int nw = max_rows_per_request < 2 ? 2 : (max_rows_per_request > CSA2_ROWS_PER_REQ_MAX ? CSA2_ROWS_PER_REQ_MAX
-                                                                                               : max_rows_per_request);
+  // A wave per row of the largest request, and at least one per part of the two
+  // summaries.
+  static_assert(2 * kSumParts <= CSA2_ROWS_PER_REQ_MAX, "summary waves fit the workgroup");
+  const int nw = max_rows_per_request < 2 * kSumParts
+                     ? 2 * kSumParts
+                     : (max_rows_per_request > CSA2_ROWS_PER_REQ_MAX ? CSA2_ROWS_PER_REQ_MAX : max_rows_per_request);
   k_write<<<dim3(g.B), dim3(64 * nw), 0, st>>>(a);
   return hipGetLastError();
 }
