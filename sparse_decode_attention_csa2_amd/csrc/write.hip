@@ -96,29 +96,32 @@ struct WriteArgs {
   uint16_t* blk_sum;
 };
 
-// Records of the entry row r completes (one wave, lane = its lane).  Every input is
-// loaded before any record is written (the stores could otherwise hold back the index
-// vector's loads).
-__device__ void write_entry(const WriteArgs& a, int r, int lane) {
-  const int b = row_request(a.g, r);
+// Records of the entry that row r of request b (rows from r0) completes; one wave, lane
+// = its lane.  Every input is loaded before any record is written (the stores could
+// otherwise hold back the index vector's loads).
+__device__ void write_entry(const WriteArgs& a, int b, int r0, int r, int lane) {
   int64_t e0, n;
   req_entries(a.g, b, e0, n);
-  int r0, r1;
-  req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
   const int64_t p = a.row_pos[r];
   const int64_t pprev = a.row_pos[r > 0 ? r - 1 : 0];
-  const bool prev_row = r - 1 >= r0 && pprev == p - 1;
-  const uint16_t* pk = prev_row ? a.kv_tok + (int64_t)(r - 1) * CSA2_D : a.ring_kv + (int64_t)b * CSA2_D;
-  const uint16_t* pi = prev_row ? a.idx_tok + (int64_t)(r - 1) * CSA2_IDX_D : a.ring_idx + (int64_t)b * CSA2_IDX_D;
+  // Both partner candidates (the previous row's tokens and the ring slot) are loaded
+  // with the row's own, so no token load waits for the positions.
+  const int rq = r > 0 ? r - 1 : 0;
   const uint16_t* xk = a.kv_tok + (int64_t)r * CSA2_D;
   const uint16_t* xi = a.idx_tok + (int64_t)r * CSA2_IDX_D;
-  const u32x4_t va = load16(pk + 8 * lane), vb = load16(xk + 8 * lane);
-  const uint32_t wa = *reinterpret_cast<const uint32_t*>(pi + 2 * lane);
+  const u32x4_t vq = load16(a.kv_tok + (int64_t)rq * CSA2_D + 8 * lane);
+  const u32x4_t vr = load16(a.ring_kv + (int64_t)b * CSA2_D + 8 * lane);
+  const u32x4_t vb = load16(xk + 8 * lane);
+  const uint32_t wq = *reinterpret_cast<const uint32_t*>(a.idx_tok + (int64_t)rq * CSA2_IDX_D + 2 * lane);
+  const uint32_t wr = *reinterpret_cast<const uint32_t*>(a.ring_idx + (int64_t)b * CSA2_IDX_D + 2 * lane);
   const uint32_t wb = *reinterpret_cast<const uint32_t*>(xi + 2 * lane);
   const f32x4a4_t gk0 = *reinterpret_cast<const f32x4a4_t*>(a.gamma_kv + 8 * lane);
   const f32x4a4_t gk1 = *reinterpret_cast<const f32x4a4_t*>(a.gamma_kv + 8 * lane + 4);
   const float gi0 = a.gamma_idx[2 * lane], gi1 = a.gamma_idx[2 * lane + 1];
   asm volatile("" ::: "memory");   // keep the loads here, ahead of the checks below
+  const bool prev_row = r - 1 >= r0 && pprev == p - 1;
+  const u32x4_t va = prev_row ? vq : vr;
+  const uint32_t wa = prev_row ? wq : wr;
   // Entry completed by the row: t = (P-1)/2 for an odd position P with t < N_b.
   if (p < 0 || (p & 1) == 0) return;
   const int64_t t = (p - 1) / 2;
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(64 * CSA2_ROWS_PER_REQ_MAX) void k_write(WriteArgs 
   if (summer) sp = summary_prepare(a, b, wave & 1, wave == 0, lane);   // wave 0 moves the ring slot
   int r0, r1;
   req_rows(a.g, b, CSA2_ROWS_PER_REQ_MAX, r0, r1);
-  for (int r = r0 + wave; r < r1; r += nw) write_entry(a, r, lane);
+  for (int r = r0 + wave; r < r1; r += nw) write_entry(a, b, r0, r, lane);
   __syncthreads();
   if (summer) {
     double s0, s1;
