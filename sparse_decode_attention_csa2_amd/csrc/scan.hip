@@ -300,16 +300,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int gi = 0; gi < kGroups; ++gi) acc[gi] = mfma16x16x32(qa[0][c], fp4x8_to_bf16(kcv[gi][c], sc[gi]), acc[gi]);
         }
+        // Two groups share one row swap: swapping group gi's partial sums (first operand)
+        // with group gi + 1's leaves rows 0 and 2 with gi's pair of rows and rows 1 and 3
+        // with gi + 1's, so lane row g adds the pair of group gi + (g & 1) for query row
+        // g >> 1 (the same two terms as a swap of each group with itself).
         const int srow = LDSK ? 0 : (g >> 1);
-        const bool real = LDSK ? g == 0 : (g & 1) == 0;
+        const bool real = LDSK ? g < 2 : true;
+        static_assert(kGroups % 2 == 0, "groups in pairs");
 #pragma unroll
-        for (int gi = 0; gi < kGroups; ++gi) {
-          float part = 0.f;
+        for (int gi = 0; gi < kGroups; gi += 2) {
+          float part[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            part = fmaf(wv[0][i], __int_as_float(max(__float_as_int(acc[gi][i]), 0)), part);
-          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-          float* dst = real ? &wst[srow * wst_ld + lb + 16 * gi + m] : &wtrash[lane];
+          for (int j = 0; j < 2; ++j) {
+            part[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              part[j] = fmaf(wv[0][i], __int_as_float(max(__float_as_int(acc[gi + j][i]), 0)), part[j]);
+          }
+          const auto sw =
+              __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+          float* dst = real ? &wst[srow * wst_ld + lb + 16 * (gi + (g & 1)) + m] : &wtrash[lane];
           *dst = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
       } else {
