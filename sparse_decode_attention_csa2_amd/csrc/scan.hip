@@ -348,9 +348,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       }
     };
     // A chunk in a slot, read in the MFMA lane layout: lane (m, g) of group gi takes
-    // entry 16gi + m's bytes 16g .. 16g+15 and its scale byte g, which one rotate (right
-    // by 8g + 9) moves to the fp32 exponent field.
-    const int srot = (8 * g + 9) & 31;
+    // entry 16gi + m's bytes 16g .. 16g+15 and its scale byte g (read as a byte and
+    // shifted into the fp32 exponent field: one instruction, against a rotate and a
+    // mask for a byte taken from the scale word).
     auto score_slot = [&](const uint32_t* kst, int lb) {
       u32x4_t kcv[kGroups];
       float sc[kGroups];
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         const int e = 16 * gi + m;   // entry of the chunk; 17 words each, a piece skipped per 4
         const uint32_t* w = kst + e * (CSA2_IDX_BYTES / 4) + 4 * (e >> 2);
         kcv[gi] = u32x4_t{w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]};
-        sc[gi] = __uint_as_float(__builtin_amdgcn_alignbit(w[16], w[16], srot) & 0x7F800000u);
+        sc[gi] = e8m0_operand(reinterpret_cast<const uint8_t*>(w + 16)[g]);   // scale byte g
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
