@@ -128,6 +128,26 @@ def test_cache_write_ragged_and_paged(csa2):
         check_write(ww, got, ref)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_cache_write_random_shapes(csa2, case):
+    # Seeded random requests: lengths from 1 entry to a few blocks (block edges included),
+    # 1 to 16 rows each, the last position even or odd, contiguous or paged pools.
+    rng = np.random.default_rng(900 + case)
+    B = int(rng.integers(1, 9))
+    lens = [int(rng.choice([rng.integers(1, 70), 64 * rng.integers(1, 40) + rng.integers(-1, 2),
+                            rng.integers(70, 5000)])) for _ in range(B)]
+    lens = [max(1, n) for n in lens]
+    rows = [min(int(rng.integers(1, 17)), 2 * n - 1) for n in lens]   # positions stay >= 0
+    wl = make_workload(f"wrand{case}", 910 + case, lens, rows_per_req=rows, n_needles=0)
+    ww = to_paged(wl, seed=920 + case) if rng.integers(0, 2) else wl
+    w = make_write_inputs(ww, 930 + case, last_even=bool(rng.integers(0, 2)))
+    _log(f"random cache write {case}: lens {lens} rows {rows} paged {ww is not wl}")
+    got = run_write(csa2, ww, w)
+    ref = oracle.cache_write(ww, w["row_pos"], w["kv_tok"], w["idx_tok"], w["ring_kv"], w["ring_idx"],
+                             w["gamma_kv"], w["gamma_idx"])
+    check_write(ww, got, ref)
+
+
 def test_written_cache_decodes_like_the_oracle(csa2):
     # Write the last entries of a verify batch, then decode over the written pools.
     from oracle import parity
