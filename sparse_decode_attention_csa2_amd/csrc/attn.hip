@@ -164,7 +164,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   __shared__ __align__(16) uint16_t Kl[TK * KLS];
   __shared__ __align__(16) float Sx[8][4 * NB][64];
   __shared__ float ksc[TK];
-  __shared__ int kval[TK];
+  __shared__ float kbias[TK];   // 0 for a key of the split, -inf for an empty slot
 
   static_assert(!(HS && HALF), "head-split launches plan whole tiles");
   constexpr int NO = HS ? 4 : 16;     // 16-dim O tiles per wave
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
       if (ch == 0) {
         const int key = 32 * u + 2 * kp + e;
         ksc[key] = kr[e].kind == 2 ? __uint_as_float(kr[e].sc) : (kr[e].kind == 1 ? 1.f : 0.f);
-        kval[key] = kr[e].kind != 0;
+        kbias[key] = kr[e].kind != 0 ? 0.f : -INFINITY;
       }
     }
     __syncthreads();
@@ -352,9 +352,10 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 16 * b + 4 * g + i;
-        const bool ok = kval[key] != 0;
         sc[4 * b + i] = ksc[key];
-        z[4 * b + i] = ok ? s[b][i] * sc[4 * b + i] * a.sm_scale_log2 : -INFINITY;
+        // An fma with a zero addend rounds like the product alone; an empty slot (zero
+        // record and scale) gets -inf.
+        z[4 * b + i] = fmaf(s[b][i] * sc[4 * b + i], a.sm_scale_log2, kbias[key]);
         mx = fmaxf(mx, z[4 * b + i]);
       }
     }
