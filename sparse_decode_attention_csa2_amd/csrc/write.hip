@@ -14,6 +14,8 @@
 // waves per block sum a quarter of the records of each block that received entries,
 // the quarters meet in LDS, one wave per block stores the summary, and one moves the
 // ring slot, which every row that reads it has read before the barrier.
+#include <climits>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -52,10 +54,56 @@ __device__ __forceinline__ double e8m0_half_scale(uint32_t e) {
 
 typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
 
+// Cross-lane steps on the VALU (no LDS round trips): lanes l and l ^ 32 / l ^ 16 through
+// gfx950's permlane swaps; within a 16-lane row, DPP rotations by 8 (lane l ^ 8) and by
+// 4, and quad permutes for l ^ 2 and l ^ 1.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;
+
+// Sum over the wave, as the butterfly over lanes l ^ 32, 16, 8, 4, 2, 1 adds it (each
+// step adds the same two values; after the step over l ^ 8, lanes l and l ^ 8 agree, so
+// the rotation by 4 reads lane l ^ 4's value).
 __device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  v += __uint_as_float(dpp<kRowRor8>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowRor4>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kQuadXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kQuadXor1>(__float_as_uint(v)));
   return v;
+}
+
+// Maximum over each 16-lane row (order does not matter for a maximum).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp<kQuadXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kQuadXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kRowRor4>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp<kRowRor8>(__float_as_uint(v))));
+}
+
+// Minimum and maximum over the wave.
+__device__ __forceinline__ void wave_minmax_i(int& lo, int& hi) {
+  const auto a32 = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
+  const auto b32 = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
+  lo = min((int)a32[0], (int)a32[1]);
+  hi = max((int)b32[0], (int)b32[1]);
+  const auto a16 = __builtin_amdgcn_permlane16_swap((uint32_t)lo, (uint32_t)lo, false, false);
+  const auto b16 = __builtin_amdgcn_permlane16_swap((uint32_t)hi, (uint32_t)hi, false, false);
+  lo = min((int)a16[0], (int)a16[1]);
+  hi = max((int)b16[0], (int)b16[1]);
+  lo = min(lo, (int)dpp<kRowRor8>((uint32_t)lo));
+  hi = max(hi, (int)dpp<kRowRor8>((uint32_t)hi));
+  lo = min(lo, (int)dpp<kRowRor4>((uint32_t)lo));
+  hi = max(hi, (int)dpp<kRowRor4>((uint32_t)hi));
+  lo = min(lo, (int)dpp<kQuadXor2>((uint32_t)lo));
+  hi = max(hi, (int)dpp<kQuadXor2>((uint32_t)hi));
+  lo = min(lo, (int)dpp<kQuadXor1>((uint32_t)lo));
+  hi = max(hi, (int)dpp<kQuadXor1>((uint32_t)hi));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -147,7 +195,7 @@ __device__ void write_entry(const WriteArgs& a, int b, int r0, int r, int lane) 
       y[i] = y[i] * rs * gk[i];
       amax = fmaxf(amax, fabsf(y[i]));
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));   // 16-dim block = lanes 2k, 2k+1
+    amax = fmaxf(amax, __uint_as_float(dpp<kQuadXor1>(__float_as_uint(amax))));   // 16-dim block = lanes 2k, 2k+1
     const int e = fp4_scale_exp(amax);
     uint32_t codes = 0u;
 #pragma unroll
@@ -164,8 +212,7 @@ __device__ void write_entry(const WriteArgs& a, int b, int r0, int r, int lane) 
     y0 = y0 * rs * gi0;
     y1 = y1 * rs * gi1;
     float amax = fmaxf(fabsf(y0), fabsf(y1));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));   // 32-dim block = 16 lanes
+    amax = row16_max(amax);   // 32-dim block = 16 lanes
     const int e = fp4_scale_exp(amax);
     const uint32_t c = e2m1_code(__builtin_ldexpf(y0, -e)) | (e2m1_code(__builtin_ldexpf(y1, -e)) << 4);
     uint8_t* rec = a.idx_k + row * CSA2_IDX_BYTES;
@@ -203,14 +250,10 @@ __device__ SummaryPrep summary_prepare(const WriteArgs& a, int b, int which, boo
     const int64_t p = a.row_pos[r0 + lane];
     tl = (p >= 0 && (p & 1) != 0 && (p - 1) / 2 < n) ? (p - 1) / 2 : -1;
   }
-  int64_t tmin = tl >= 0 ? tl : INT64_MAX, tmax = tl;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int64_t om = __shfl_xor(tmin, m, 64), ox = __shfl_xor(tmax, m, 64);
-    tmin = om < tmin ? om : tmin;
-    tmax = ox > tmax ? ox : tmax;
-  }
-  if (tmin != INT64_MAX) {
+  // Entries are below max_entries (32 bits).
+  int tmin = tl >= 0 ? (int)tl : INT_MAX, tmax = (int)tl;
+  wave_minmax_i(tmin, tmax);
+  if (tmin != INT_MAX) {
     const int64_t j = tmin / CSA2_BLOCK + which;
     if (j <= tmax / CSA2_BLOCK && j < nb) {
       // A block's entries are consecutive pool rows (a page, with paged pools).
