@@ -482,9 +482,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   constexpr int64_t kStride = 8 * 16 * 256;   // floats per split
   constexpr int kBatch = KB;
   f32x4_t v[kBatch];
+  // Every load issues (clamped to the launch's last split; only u < ns are used): a
+  // guarded load made the compiler wait for the first ones before issuing the rest.
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u)   // every launched split has a partial slot; only u < ns are used
-    v[u] = u < a.splits ? *reinterpret_cast<const f32x4_t*>(src + u * kStride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < kBatch; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(src + min(u, a.splits - 1) * kStride);
   __syncthreads();
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, msh[s][ln]);
