@@ -478,7 +478,8 @@ struct SliceBufs {
 
 static size_t decode_layout(const csa2_decode_args* a, char* base, float** scores, float** blk_scores,
                             int32_t** kept, int32_t** n_kept, int32_t** sel, int32_t** n_sel, int32_t** sel_rows,
-                            char** attn_ws, size_t* attn_bytes, SliceBufs* slices = nullptr) {
+                            char** attn_ws, size_t* attn_bytes, SliceBufs* slices = nullptr,
+                            uint16_t** q_mx = nullptr) {
   const csa2_ragged& rg = a->rg;
   const int64_t R = rg.num_rows;
   const int64_t ld = round_up((size_t)(rg.max_entries > 0 ? rg.max_entries : 1), 64);
@@ -514,6 +515,9 @@ static size_t decode_layout(const csa2_decode_args* a, char* base, float** score
     int32_t* cn = c.take<int32_t>((size_t)R * nsl);
     if (slices) *slices = SliceBufs{nsl, cb, cs, cn};
   }
+  // MXFP8 route: the rounded query, written by the selection launch.
+  uint16_t* qm = a->qp_route == CSA2_QP_MXFP8 ? c.take<uint16_t>((size_t)R * CSA2_HEADS * CSA2_D) : nullptr;
+  if (q_mx) *q_mx = qm;
   return round_up(c.used, 256);
 }
 
@@ -552,8 +556,9 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   char* attn_ws;
   size_t attn_bytes;
   SliceBufs slices;
+  uint16_t* q_mx;
   decode_layout(a, static_cast<char*>(ws), &scores, &blk_scores, &kept, &n_kept, &sel, &n_sel, &sel_rows, &attn_ws,
-                &attn_bytes, &slices);
+                &attn_bytes, &slices, &q_mx);
   const int64_t ld = a->scores ? a->scores_ld : (int64_t)round_up((size_t)(g.max_entries > 0 ? g.max_entries : 1), 64);
   const int64_t blk_ld = (int64_t)round_up((size_t)(blocks_of(g.max_entries) > 0 ? blocks_of(g.max_entries) : 1), 64);
 
@@ -564,6 +569,12 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
                   a->out, a->lse, attn_ws, attn_bytes, at));
   at.sel_rows = sel_rows ? 1 : 0;
   at.qp_route = a->qp_route;
+  if (q_mx) {
+    // The query is rounded once per row by the selection launch (in parallel with it)
+    // instead of in every attention workgroup.
+    at.q = q_mx;
+    at.q_rounded = 1;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   ScanArgs sa{};
@@ -596,6 +607,8 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   se.cand_blk = slices.blk;
   se.cand_sc = slices.sc;
   se.cand_n = slices.n;
+  se.q = a->q;
+  se.q_mx = q_mx;
 
   auto mark = [&](int i) -> hipError_t {
     return a->events ? hipEventRecord(static_cast<hipEvent_t>(a->events[i]), st) : hipSuccess;

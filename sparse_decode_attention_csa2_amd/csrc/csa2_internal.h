@@ -152,6 +152,11 @@ struct SelectArgs {
   int32_t* cand_blk;
   float* cand_sc;
   int32_t* cand_n;
+  // MXFP8 route: the query [R][64][512] bf16, and where its MXFP8-rounded copy goes
+  // (nullable: no rounding).  The selection launch that precedes attention rounds it in
+  // extra workgroups (16 heads each), beside the rows' own workgroups.
+  const uint16_t* q;
+  uint16_t* q_mx;
 };
 
 // Blocks per slice of the sliced coarse stage, and when it is used: rows with more than
@@ -194,6 +199,7 @@ struct AttnArgs {
   float* out;                // [R][64][512]
   float* lse;                // [R][64]
   int32_t head_split;        // 1: four workgroups per split, one per head group
+  int32_t q_rounded;         // MXFP8 route: q already holds the MXFP8-rounded query
 };
 
 void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits,

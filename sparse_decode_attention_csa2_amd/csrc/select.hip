@@ -603,6 +603,21 @@ __device__ void fine(const SelectArgs& a, int r, int64_t n, int64_t e0, int nk, 
   if (threadIdx.x == 0) a.n_sel[r] = take;
 }
 
+// MXFP8 route: workgroup `part` (4 per row) rounds 16 heads of its row's query; wave w
+// takes one head, lane l its 8 dims at 32 (l & 15) + 8 (l >> 4), so that the lanes l,
+// l ^ 16, l ^ 32 and l ^ 48 hold one 32-dim block between them.
+constexpr int kQParts = CSA2_HEADS / (NT / 64);
+static_assert(kQParts * (NT / 64) == CSA2_HEADS, "whole heads per workgroup");
+__device__ __forceinline__ void round_query_part(const SelectArgs& a, int part) {
+  const int r = part / kQParts;
+  const int head = (part % kQParts) * (NT / 64) + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t off = ((int64_t)r * CSA2_HEADS + head) * CSA2_D + 32 * (lane & 15) + 8 * (lane >> 4);
+  const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(a.q + off);
+  *reinterpret_cast<bf16x8_t*>(a.q_mx + off) = mx8_round_block_bf16(x);
+}
+__host__ __device__ inline int query_parts(const SelectArgs& a) { return a.q_mx ? kQParts * a.g.R : 0; }
+
 template <bool PAGED, bool BIG>
 __global__ __launch_bounds__(NT) void k_block_select(SelectArgs a) {
   __shared__ SelShared sh;
@@ -614,11 +629,16 @@ __global__ __launch_bounds__(NT) void k_block_select(SelectArgs a) {
   coarse<BIG>(a, blockIdx.x, nb, sh, kbuf, pre);
 }
 
-template <bool PAGED>
+// QR: the launch also carries the MXFP8 query-rounding workgroups (after the rows').
+template <bool PAGED, bool QR>
 __global__ __launch_bounds__(NT) void k_topk(SelectArgs a, int all_entries) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kMaxCand];
   const int r = blockIdx.x;
+  if (QR && r >= a.g.R) {
+    round_query_part(a, r - a.g.R);
+    return;
+  }
   int64_t n, e0;
   row_blocks<PAGED>(a, r, n, e0);
   int nk = 0;
@@ -665,12 +685,16 @@ __global__ __launch_bounds__(NT) void k_block_slices(SelectArgs a) {
 // blocks than LDS holds; 2: the sliced coarse stage's candidates; 3: as 0 for rows of at
 // most kSmallRowBlocks block slots, whose whole gather is one round of loads (a batch
 // sized for more blocks would issue loads that only repeat the last slot).
-template <bool PAGED, int CMODE>
+template <bool PAGED, int CMODE, bool QR>
 __global__ __launch_bounds__(NT) void k_select_fused(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t kbuf[kLdsBlocks];
   constexpr int GBC = CMODE == 3 ? kSmallRowBlocks / NT : kGB;
   const int r = blockIdx.x;
+  if (QR && r >= a.g.R) {
+    round_query_part(a, r - a.g.R);
+    return;
+  }
   float pre[GBC];
   if (CMODE == 0 || CMODE == 3) prefetch_blocks(a, r, pre);
   int64_t n, e0;
@@ -697,34 +721,45 @@ hipError_t launch_block_select(SelectArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool QR>
+hipError_t topk_launch(SelectArgs a, bool all_entries, hipStream_t st) {
+  const dim3 grid(a.g.R + query_parts(a));
+  if (a.g.page_table)
+    k_topk<true, QR><<<grid, dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
+  else
+    k_topk<false, QR><<<grid, dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(SelectArgs a, bool all_entries, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-  if (a.g.page_table)
-    k_topk<true><<<dim3(a.g.R), dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
-  else
-    k_topk<false><<<dim3(a.g.R), dim3(NT), 0, st>>>(a, all_entries ? 1 : 0);
+  return a.q_mx ? topk_launch<true>(a, all_entries, st) : topk_launch<false>(a, all_entries, st);
+}
+
+#ifndef CSA2_SEL_SMALL_ROWS
+#define CSA2_SEL_SMALL_ROWS 1
+#endif
+template <bool QR>
+hipError_t select_fused_launch(SelectArgs a, hipStream_t st) {
+  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : (CSA2_SEL_SMALL_ROWS && a.blk_ld <= kSmallRowBlocks ? 3 : 0));
+  const dim3 grid(a.g.R + query_parts(a)), block(NT);
+  if (a.g.page_table) {
+    if (mode == 2) k_select_fused<true, 2, QR><<<grid, block, 0, st>>>(a);
+    else if (mode == 1) k_select_fused<true, 1, QR><<<grid, block, 0, st>>>(a);
+    else if (mode == 3) k_select_fused<true, 3, QR><<<grid, block, 0, st>>>(a);
+    else k_select_fused<true, 0, QR><<<grid, block, 0, st>>>(a);
+  } else {
+    if (mode == 2) k_select_fused<false, 2, QR><<<grid, block, 0, st>>>(a);
+    else if (mode == 1) k_select_fused<false, 1, QR><<<grid, block, 0, st>>>(a);
+    else if (mode == 3) k_select_fused<false, 3, QR><<<grid, block, 0, st>>>(a);
+    else k_select_fused<false, 0, QR><<<grid, block, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_select_fused(SelectArgs a, hipStream_t st) {
   if (a.g.R == 0) return hipSuccess;
-#ifndef CSA2_SEL_SMALL_ROWS
-#define CSA2_SEL_SMALL_ROWS 1
-#endif
-  const int mode = a.n_slices > 0 ? 2 : (a.blk_ld > kLdsBlocks ? 1 : (CSA2_SEL_SMALL_ROWS && a.blk_ld <= kSmallRowBlocks ? 3 : 0));
-  const dim3 grid(a.g.R), block(NT);
-  if (a.g.page_table) {
-    if (mode == 2) k_select_fused<true, 2><<<grid, block, 0, st>>>(a);
-    else if (mode == 1) k_select_fused<true, 1><<<grid, block, 0, st>>>(a);
-    else if (mode == 3) k_select_fused<true, 3><<<grid, block, 0, st>>>(a);
-    else k_select_fused<true, 0><<<grid, block, 0, st>>>(a);
-  } else {
-    if (mode == 2) k_select_fused<false, 2><<<grid, block, 0, st>>>(a);
-    else if (mode == 1) k_select_fused<false, 1><<<grid, block, 0, st>>>(a);
-    else if (mode == 3) k_select_fused<false, 3><<<grid, block, 0, st>>>(a);
-    else k_select_fused<false, 0><<<grid, block, 0, st>>>(a);
-  }
-  return hipGetLastError();
+  return a.q_mx ? select_fused_launch<true>(a, st) : select_fused_launch<false>(a, st);
 }
 
 hipError_t launch_block_slices(SelectArgs a, hipStream_t st) {
