@@ -573,7 +573,6 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
     // The query is rounded once per row by the selection launch (in parallel with it)
     // instead of in every attention workgroup.
     at.q = q_mx;
-    at.q_rounded = 1;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 

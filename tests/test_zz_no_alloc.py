@@ -62,12 +62,13 @@ def _poison(d):
 def test_static_decode_matches_decode_twice_then_smaller(lib):
     # Two static calls in a row, the second on a smaller batch (the buffer then still
     # holds the first call's contents); each is compared bit for bit with csa2_decode on
-    # the same inputs, with the outputs poisoned before every call.
-    for cfg in (3, 0):
+    # the same inputs, with the outputs poisoned before every call; both Q/P routes (the
+    # MXFP8 route's workspace also holds the rounded query).
+    for route, cfg in ((csa2.QP_BF16, 3), (csa2.QP_BF16, 0), (csa2.QP_MXFP8, 3), (csa2.QP_MXFP8, 0)):
         wl = make_config(cfg)
         dw = upload(wl)
-        d = csa2.Decoder(*dw.decode_inputs(), k=wl.k, n_keep=wl.n_keep, sm_scale=wl.sm_scale)
-        _log(f"static decode, {wl.name}: {wl.num_rows} rows, workspace {d.ws_bytes} bytes "
+        d = csa2.Decoder(*dw.decode_inputs(), k=wl.k, n_keep=wl.n_keep, sm_scale=wl.sm_scale, qp_route=route)
+        _log(f"static decode, {wl.name}, route {route}: {wl.num_rows} rows, workspace {d.ws_bytes} bytes "
              f"(static buffer {csa2.STATIC_WS_BYTES})")
         assert d.ws_bytes <= csa2.STATIC_WS_BYTES
         _poison(d)
