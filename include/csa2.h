@@ -227,9 +227,10 @@ typedef struct csa2_decode_args {
   void* const* events;         /* nullable: CSA2_DECODE_EVENTS hipEvent_t handles, recorded on `stream`
                                   before the first kernel and after each stage (scan, select,
                                   attention, merge) for per-stage timing; recording adds no sync */
-  int32_t qp_route;            /* CSA2_QP_BF16 (default) or CSA2_QP_MXFP8; with MXFP8 the
-                                  workspace also holds the rounded query (64 KB per row),
-                                  which the selection launch writes and attention reads */
+  int32_t qp_route;            /* CSA2_QP_BF16 (default) or CSA2_QP_MXFP8; with MXFP8 and few
+                                  rows the workspace also holds the rounded query (64 KB
+                                  per row), which the selection launch writes and attention
+                                  reads */
 } csa2_decode_args;
 
 #define CSA2_DECODE_EVENTS 5

@@ -515,8 +515,12 @@ static size_t decode_layout(const csa2_decode_args* a, char* base, float** score
     int32_t* cn = c.take<int32_t>((size_t)R * nsl);
     if (slices) *slices = SliceBufs{nsl, cb, cs, cn};
   }
-  // MXFP8 route: the rounded query, written by the selection launch.
-  uint16_t* qm = a->qp_route == CSA2_QP_MXFP8 ? c.take<uint16_t>((size_t)R * CSA2_HEADS * CSA2_D) : nullptr;
+  // MXFP8 route with a head-split attention plan (few rows): the rounded query, written
+  // by the selection launch.  Larger launches round it inside the attention, where the
+  // first tile's record loads hide that work.
+  int32_t p_tk, p_sk, p_splits, p_hs;
+  attn_plan(R, a->k, p_tk, p_sk, p_splits, p_hs);
+  uint16_t* qm = a->qp_route == CSA2_QP_MXFP8 && p_hs ? c.take<uint16_t>((size_t)R * CSA2_HEADS * CSA2_D) : nullptr;
   if (q_mx) *q_mx = qm;
   return round_up(c.used, 256);
 }
@@ -573,6 +577,7 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
     // The query is rounded once per row by the selection launch (in parallel with it)
     // instead of in every attention workgroup.
     at.q = q_mx;
+    at.q_rounded = 1;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 

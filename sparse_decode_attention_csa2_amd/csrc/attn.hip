@@ -245,6 +245,15 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
     }
   };
   load_keys(k_begin);
+  if constexpr (MX) {
+    // MXFP8 route, unless the selection launch before this one rounded the query
+    // already: block st of 32 dims = this lane's 8 values and those of lanes xor 16 and
+    // xor 32 (rounded while the first tile's records are in flight).
+    if (!a.q_rounded) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) qb[st] = mx8_round_block_bf16(qb[st]);
+    }
+  }
 
   // Kl offsets with the swizzle (kl_col) folded in.  QK^T: lane (g, ln) reads dims 8g..
   // of a 32-dim chunk of row 16b + ln, whose swizzle term is (ln >> 2) & 3 for every b.

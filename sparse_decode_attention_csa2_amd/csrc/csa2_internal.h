@@ -186,7 +186,7 @@ struct AttnArgs {
   const int32_t* n_sel;
   int32_t sel_ld;
   int32_t sel_rows;
-  int32_t qp_route;          // CSA2_QP_BF16 or CSA2_QP_MXFP8 (q: the MXFP8-rounded query)
+  int32_t qp_route;          // CSA2_QP_BF16 or CSA2_QP_MXFP8
   const uint8_t* swa;
   const float* swa_scale;
   float sm_scale_log2;       // sm_scale * log2(e)
@@ -199,6 +199,7 @@ struct AttnArgs {
   float* out;                // [R][64][512]
   float* lse;                // [R][64]
   int32_t head_split;        // 1: four workgroups per split, one per head group
+  int32_t q_rounded;         // MXFP8 route: q already holds the MXFP8-rounded query
 };
 
 void attn_plan(int64_t R, int32_t sel_ld, int32_t& tile_keys, int32_t& split_keys, int32_t& splits,
